@@ -1,0 +1,286 @@
+"""Benchmark of the GQA forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the hot path over one batch of synthetic input, with
+inputs already resident in HBM.  The default workload is the split-KV decode
+(B=16, Hq=32, Hkv=8, Skv=8192, d=128, TILE_S_KV=1024: partial kernel + merge
+kernel); `value` is its K/V-stream throughput in GB/s of algorithmic bytes
+(Q + K + V read once, O written once).  The same JSON line also carries:
+
+* roofline: the dominant kernel (the split-KV partial kernel) timed alone
+  with HIP events on its own stream, algorithmic bytes per launch over its
+  mean duration, against MI355X's 8 TB/s HBM peak;
+* secondary: the other named workloads (short-q/long-kv prefill, causal
+  prefill, ragged paged, tiny prefill), each timed the same way with its own
+  roofline fraction;
+* cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
+  sample of the decode workload.
+
+One GPU only: --gpus above 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "GQA attn prefill TFLOP/s & decode KV GB/s at 1 GPU, % of MI355X peak"
+
+
+def gqa():
+    import gqa_attention_forward_amd as m
+    return m
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def dense_bytes(c, kv_len=None):
+    """Q + true K/V rows + O, each once (bf16)."""
+    n = c.Skv if kv_len is None else kv_len
+    q = c.B * c.Hq * c.Sq * c.d * 2
+    kv = 2 * c.B * c.Hkv * n * c.d * 2
+    return q + kv + q, q + kv
+
+
+def dense_flops(c):
+    """4 d flops per visible (query, key) pair; causal counts j <= i only."""
+    if c.causal:
+        pairs = c.B * c.Hq * sum(min(c.Skv, c.Skv - c.Sq + i + 1) for i in range(c.Sq))
+    else:
+        pairs = c.B * c.Hq * c.Sq * c.Skv
+    return 4 * c.d * pairs
+
+
+def paged_work(w):
+    ql = w["q_len"].numpy().astype(np.int64)
+    kl = w["kv_len"].numpy().astype(np.int64)
+    Hq, Hkv, d = w["Hq"], w["Hkv"], w["d"]
+    bytes_ = int((2 * ql * Hq * d * 2).sum() + (2 * kl * Hkv * d * 2).sum())
+    flops = int((4 * d * Hq * ql * kl).sum())
+    return bytes_, flops
+
+
+# ---------------------------------------------------------------- timing
+
+def time_loop(fn, steps, warmup, stream):
+    """Mean ms per call of `fn` over `steps` calls on `stream` (HIP events)."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def roof(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+# ---------------------------------------------------------------- workloads
+
+def setup_dense(name, device):
+    c = workloads.CASES[name]
+    inp = workloads.make_case(c)
+    g = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    return c, inp, g
+
+
+def decode_step_fns(g, c):
+    m = gqa()
+    out = torch.empty_like(g["q"])
+    ns = m.n_splits(c.Skv, c.tile_s_kv)
+    ws = torch.empty(m.workspace_size(c.B, c.Hq, 1, c.Skv, c.d, c.tile_s_kv), dtype=torch.uint8,
+                     device=g["q"].device)
+
+    def step():
+        m.decode_splitkv(g["q"], g["k"], g["v"], kv_len=g["kv_len"], scale=g["scale"],
+                         tile_s_kv=c.tile_s_kv, out=out, workspace=ws)
+
+    def partial():
+        m.splitkv_partial(g["q"], g["k"], g["v"], tile_s_kv=c.tile_s_kv, kv_len=g["kv_len"],
+                          scale=g["scale"], workspace=ws)
+
+    def merge():
+        m.splitkv_merge(ws, B=c.B, Hq=c.Hq, Sq=1, d=c.d, n_split=ns, out=out)
+
+    return step, partial, merge, out
+
+
+def prefill_step_fn(g, c, tile=0):
+    m = gqa()
+    out = torch.empty_like(g["q"])
+    ws = None
+    if tile:
+        ws = torch.empty(m.workspace_size(c.B, c.Hq, c.Sq, c.Skv, c.d, tile), dtype=torch.uint8,
+                         device=g["q"].device)
+
+    def step():
+        m.prefill(g["q"], g["k"], g["v"], kv_len=g["kv_len"], scale=g["scale"], causal=c.causal,
+                  tile_s_kv=tile, out=out, workspace=ws)
+
+    return step, out
+
+
+def bench_decode(args, device, stream):
+    c, inp, g = setup_dense("decode_splitkv", device)
+    step, partial, merge, out = decode_step_fns(g, c)
+    ms = time_loop(step, args.steps, args.warmup, stream)
+    total_bytes, read_bytes = dense_bytes(c)
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    # dominant kernel alone: the split-KV partial kernel (reads Q, K, V once)
+    ms_p = time_loop(partial, args.steps, max(1, args.warmup // 2), stream)
+    ms_m = time_loop(merge, args.steps, 1, stream)
+    assert torch.isfinite(out.float()).all()
+    return c, inp, {
+        "ms_per_step": ms, "value": gbs, "total_bytes": total_bytes,
+        "roofline": roof("hbm", read_bytes / (ms_p * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "kernel_ms": {"partial": round(ms_p, 5), "merge": round(ms_m, 5)},
+        "kernel_bytes_per_launch": {"partial": read_bytes},
+    }
+
+
+def bench_secondary(args, device, stream):
+    res = {}
+    steps = max(3, min(args.steps, 20))
+    # short-q / long-kv prefill (HBM-bound): split-KV, 8 splits of 2048 keys
+    c, _, g = setup_dense("shortq_longkv", device)
+    for tile in (0, 2048):
+        step, out = prefill_step_fn(g, c, tile)
+        ms = time_loop(step, steps, 2, stream)
+        tb, _ = dense_bytes(c)
+        fl = dense_flops(c)
+        res[f"shortq_longkv_tile{tile}"] = {
+            "ms": round(ms, 5), "GB/s": round(tb / (ms * 1e-3) / 1e9, 1),
+            "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+            "roofline": roof("hbm", tb / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    del g, out
+    # causal prefill (MFMA-bound)
+    c, _, g = setup_dense("causal_prefill", device)
+    step, out = prefill_step_fn(g, c, 0)
+    ms = time_loop(step, steps, 2, stream)
+    fl = dense_flops(c)
+    res["causal_prefill"] = {
+        "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2), "flops": fl,
+        "roofline": roof("mfma", fl / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s")}
+    del g, out
+    # ragged paged with sink (launch-bound)
+    w = workloads.make_paged()
+    gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
+    m = gqa()
+    outp = torch.empty_like(gw["q"])
+
+    def pstep():
+        m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"], gw["page_table"],
+                gw["kv_len"], max_q_len=w["max_q_len"], scale=w["scale"], sink=gw["sink"],
+                out=outp)
+    ms = time_loop(pstep, steps, 2, stream)
+    pb, pf = paged_work(w)
+    t_roof = max(pb / (HBM_PEAK_GBS * 1e9), pf / (BF16_PEAK_TFLOPS * 1e12))
+    res["ragged_paged"] = {"ms": round(ms, 5), "bytes": pb, "flops": pf,
+                           "roofline_frac": round(t_roof / (ms * 1e-3), 4)}
+    # tiny prefill (launch-bound)
+    c, _, g = setup_dense("tiny_prefill", device)
+    step, out = prefill_step_fn(g, c, 0)
+    ms = time_loop(step, steps, 2, stream)
+    res["tiny_prefill"] = {"ms": round(ms, 5)}
+    return res
+
+
+def cpu_baseline(inp, c, budget_s):
+    """The oracle on this host's cores over whole decode sequences until ~budget_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    elapsed, done = 0.0, 0
+    q = inp["q"]
+    k, v = inp["k"], inp["v"]
+    while done < c.B and elapsed < budget_s:
+        qb = q[done:done + 1].to(torch.float64).numpy()
+        kb = k[done:done + 1].to(torch.float64).numpy()
+        vb = v[done:done + 1].to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        oracle.attention_fp64(qb, kb, vb, scale=inp["scale"])
+        elapsed += time.perf_counter() - t0
+        done += 1
+    per_seq = (2 * c.Hq * c.d * 2) + 2 * c.Hkv * c.Skv * c.d * 2
+    return {"value": round(done * per_seq / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {c.B} decode sequences (all {c.Hq} heads x {c.Skv} keys each), "
+                      f"{elapsed:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device)
+    torch.cuda.synchronize()
+
+    c, inp, dec = bench_decode(args, device, stream)
+    secondary = None if args.no_secondary else bench_secondary(args, device, stream)
+    cpu = cpu_baseline(inp, c, args.cpu_budget) if args.cpu_budget > 0 else None
+
+    line = {
+        "metric": METRIC,
+        "value": round(dec["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_splitkv", "B": c.B, "Hq": c.Hq, "Hkv": c.Hkv, "Sq": 1,
+                   "Skv": c.Skv, "d": c.d, "tile_s_kv": c.tile_s_kv,
+                   "seq_len": c.Skv, "global_batch": c.B, "parallelism": "none (1 GPU)"},
+        "roofline": dec["roofline"],
+        "kernel_ms": dec["kernel_ms"],
+        "kernel_bytes_per_launch": dec["kernel_bytes_per_launch"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+"""Grouped-query attention forward for AMD MI355X (gfx950) -- Python binding.
+
+Thin wrappers over the C ABI in include/gqa.h (libgqa.so, loaded with
+ctypes).  PyTorch supplies device memory and the current stream only; every
+step of the attention runs in the library's HIP kernels.  There is no CPU or
+eager fallback: without the built library every call raises.
+
+    prefill(q, k, v, ...)          dense [B, H, S, d] tensors, one pass or split-KV
+    decode_splitkv(q, k, v, ...)   Sq = 1, split-KV partials + merge kernel
+    splitkv_partial / splitkv_merge  the two split-KV phases on their own
+    paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, ...)
+    workspace_size(...)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import (GQAError, GQAInvalidArgument, GQAUnsupported,  # noqa: F401
+                   GQAWorkspaceError)
+
+__all__ = ["prefill", "decode_splitkv", "splitkv_partial", "splitkv_merge", "paged",
+           "workspace_size", "n_splits", "GQAError"]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_dev(name, t, dtype):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _bhsd(name, t):
+    _need_dev(name, t, torch.bfloat16)
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, S, d]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous head dim")
+
+
+def _scale(scale, d):
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32)) if scale is None else float(scale)
+
+
+def n_splits(Skv: int, tile_s_kv: int) -> int:
+    return max(1, -(-int(Skv) // int(tile_s_kv))) if tile_s_kv > 0 else 1
+
+
+def workspace_size(B, Hq, Sq, Skv, d, tile_s_kv) -> int:
+    out = ctypes.c_size_t(0)
+    _lib.check(_lib.load().gqa_attention_workspace_size(B, Hq, Sq, Skv, d, tile_s_kv,
+                                                        ctypes.byref(out)))
+    return int(out.value)
+
+
+def _workspace(device, nbytes, workspace):
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def prefill(q, k, v, *, kv_len=None, scale=None, sink=None, causal=False, tile_s_kv=0,
+            out=None, workspace=None):
+    """O = softmax(scale Q K^T + mask [+ sink]) V for dense [B, H, S, d] bf16 tensors."""
+    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
+    _need_dev("kv_len", kv_len, torch.int32)
+    _need_dev("sink", sink, torch.float32)
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _bhsd("out", out)
+    nbytes = workspace_size(B, Hq, Sq, Skv, d, tile_s_kv)
+    workspace = _workspace(q.device, nbytes, workspace)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.gqa_attention_prefill(
+        _ptr(q), _lib.strides3(q.stride()[:3]), _ptr(k), _lib.strides3(k.stride()[:3]),
+        _ptr(v), _lib.strides3(v.stride()[:3]), _ptr(out), _lib.strides3(out.stride()[:3]),
+        B, Hq, Hkv, Sq, Skv, d, _ptr(kv_len), _scale(scale, d), _ptr(sink), int(bool(causal)),
+        int(tile_s_kv), _ptr(workspace), wsb, _stream(q.device)))
+    return out
+
+
+def decode_splitkv(q, k, v, *, kv_len=None, scale=None, sink=None, tile_s_kv=1024, out=None,
+                   workspace=None):
+    """Single-token decode: q [B, Hq, 1, d]; split-KV partials then the merge kernel."""
+    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
+    _need_dev("kv_len", kv_len, torch.int32)
+    _need_dev("sink", sink, torch.float32)
+    B, Hq, Sq, d = q.shape
+    if Sq != 1:
+        raise ValueError("decode_splitkv takes one query row per (b, h)")
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    nbytes = workspace_size(B, Hq, 1, Skv, d, tile_s_kv)
+    workspace = _workspace(q.device, nbytes, workspace)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.gqa_attention_decode_splitkv(
+        _ptr(q), _lib.strides3(q.stride()[:3]), _ptr(k), _lib.strides3(k.stride()[:3]),
+        _ptr(v), _lib.strides3(v.stride()[:3]), _ptr(out), _lib.strides3(out.stride()[:3]),
+        B, Hq, Hkv, Skv, d, _ptr(kv_len), _scale(scale, d), _ptr(sink), int(tile_s_kv),
+        _ptr(workspace), wsb, _stream(q.device)))
+    return out
+
+
+def splitkv_partial(q, k, v, *, tile_s_kv, kv_len=None, scale=None, causal=False,
+                    workspace=None):
+    """Partial states only; returns (ml [rows, n_split, 2], ot [rows, n_split, d], workspace)."""
+    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
+    _need_dev("kv_len", kv_len, torch.int32)
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    nbytes = workspace_size(B, Hq, Sq, Skv, d, tile_s_kv)
+    workspace = _workspace(q.device, nbytes, workspace)
+    wsb = workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.gqa_attention_splitkv_partial(
+        _ptr(q), _lib.strides3(q.stride()[:3]), _ptr(k), _lib.strides3(k.stride()[:3]),
+        _ptr(v), _lib.strides3(v.stride()[:3]), B, Hq, Hkv, Sq, Skv, d, _ptr(kv_len),
+        _scale(scale, d), int(bool(causal)), int(tile_s_kv), _ptr(workspace), wsb,
+        _stream(q.device)))
+    rows, ns = B * Hq * Sq, n_splits(Skv, tile_s_kv)
+    flat = workspace.view(torch.float32)
+    ml = flat[: rows * ns * 2].view(rows, ns, 2)
+    ot = flat[rows * ns * 2: rows * ns * (2 + d)].view(rows, ns, d)
+    return ml, ot, workspace
+
+
+def splitkv_merge(workspace, *, B, Hq, Sq, d, n_split, sink=None, out=None, device=None):
+    """Merge n_split partial states per row from `workspace` into bf16 O [B, Hq, Sq, d]."""
+    _need_dev("sink", sink, torch.float32)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, d), dtype=torch.bfloat16, device=workspace.device)
+    _bhsd("out", out)
+    lib = _lib.load()
+    _lib.check(lib.gqa_attention_splitkv_merge(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _lib.strides3(out.stride()[:3]), B, Hq, Sq, d, n_split, _ptr(sink),
+        _stream(workspace.device)))
+    return out
+
+
+def paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, *, max_q_len, scale=None,
+          sink=None, causal=False, page_size=64, out=None):
+    """Ragged-Q paged-KV attention: q [total_q, Hq, d]; pools [n_pages, 64, Hkv, d]."""
+    _need_dev("q", q, torch.bfloat16)
+    _need_dev("k_cache", k_cache, torch.bfloat16)
+    _need_dev("v_cache", v_cache, torch.bfloat16)
+    _need_dev("cu_seqlens_q", cu_seqlens_q, torch.int32)
+    _need_dev("page_table", page_table, torch.int32)
+    _need_dev("kv_len", kv_len, torch.int32)
+    _need_dev("sink", sink, torch.float32)
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [total_q, Hq, d] with a contiguous head dim")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_cache.dim() != 4 or k_cache.stride(3) != 1:
+        raise ValueError("caches must be [n_pages, page_size, Hkv, d] with a contiguous head dim")
+    if page_table.dim() != 2 or page_table.stride(1) != 1 or page_table.stride(0) != page_table.shape[1]:
+        raise ValueError("page_table must be a contiguous [B, max_pages] int32 tensor")
+    total_q, Hq, d = q.shape
+    B = cu_seqlens_q.numel() - 1
+    Hkv = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    lib = _lib.load()
+    _lib.check(lib.gqa_attention_paged(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache),
+        k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(page_table),
+        page_table.shape[1], _ptr(kv_len), _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv,
+        d, int(page_size), total_q, int(max_q_len), _scale(scale, d), _ptr(sink),
+        int(bool(causal)), _stream(q.device)))
+    return out

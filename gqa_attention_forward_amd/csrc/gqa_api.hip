@@ -1,0 +1,379 @@
+// Host side of libgqa: argument validation, work planning and kernel launch
+// behind the C ABI declared in include/gqa.h.
+//
+// Validation follows the AstrAI commit log's binding checks (q-head/kv-head
+// divisibility, head-dim contiguity, split-KV scratch layout validated before
+// launch) and its NULL-means-absent convention for optional pointers.  Every
+// check runs before anything is enqueued; the library never allocates,
+// synchronises or reads device memory from the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+
+#include "attn_kernels.hpp"
+#include "gqa.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gqa_status_t fail(gqa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+gqa_status_t ok() {
+  g_err[0] = '\0';
+  return GQA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// (b, h, s) element strides of a bf16 tensor must keep 16-byte rows aligned.
+gqa_status_t check_strides(const char* name, const int64_t* st, int n) {
+  if (!st) return fail(GQA_ERR_INVALID_ARGUMENT, "%s strides are NULL", name);
+  for (int i = 0; i < n; ++i) {
+    if (st[i] < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "%s stride %d is negative", name, i);
+    if (st[i] % 8 != 0)
+      return fail(GQA_ERR_UNSUPPORTED, "%s stride %d (%lld) is not a multiple of 8 elements",
+                  name, i, (long long)st[i]);
+  }
+  return GQA_OK;
+}
+
+gqa_status_t check_ptr(const char* name, const void* p) {
+  if (!p) return fail(GQA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(GQA_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  return GQA_OK;
+}
+
+gqa_status_t check_scale(float scale) {
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
+  return GQA_OK;
+}
+
+gqa_status_t check_heads(int32_t Hq, int32_t Hkv, int32_t d) {
+  if (Hq < 1 || Hkv < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "Hq and Hkv must be >= 1");
+  if (Hq % Hkv != 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  return GQA_OK;
+}
+
+size_t workspace_bytes_for(int64_t rows, int64_t n_split, int64_t d) {
+  const int64_t raw = rows * n_split * (d + 2) * 4;
+  return (size_t)((raw + 255) / 256 * 256);
+}
+
+#define GQA_TRY(...)                     \
+  do {                                   \
+    gqa_status_t st_ = (__VA_ARGS__);    \
+    if (st_ != GQA_OK) return st_;       \
+  } while (0)
+
+// ---------------------------------------------------------------- launching
+
+gqa_status_t check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return GQA_OK;
+}
+
+template <int D, int NR, int NK, int BKW, bool PAGED, bool PARTIAL>
+gqa_status_t launch_attn(gqa::AttnArgs args, int64_t q_rows_per_bg, hipStream_t stream) {
+  using C = gqa::Cfg<D, NR, NK, BKW>;
+  auto* kern = &gqa::attn_fwd_kernel<D, NR, NK, BKW, PAGED, PARTIAL>;
+  // dynamic LDS above 64 KiB has to be allowed once per kernel instantiation
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  });
+  if (attr_err != hipSuccess)
+    return fail(GQA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
+  args.n_qtiles = (int32_t)cdiv(q_rows_per_bg, NR * 32);
+  const int64_t nblocks = (int64_t)args.B * args.Hkv * args.n_split * args.n_qtiles;
+  if (nblocks <= 0) return GQA_OK;
+  if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large (%lld)", (long long)nblocks);
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::NT), C::LDS_BYTES, stream, args);
+  return check_launch("attention kernel");
+}
+
+// Wave layout by query rows per (b, kv head): decode-like groups (<= 32 rows)
+// put the waves on different keys of a shared tile, large groups put them on
+// different rows.
+template <int D, bool PAGED, bool PARTIAL>
+gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+  if (rows <= 32) return launch_attn<D, 1, 2, 32, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 64) return launch_attn<D, 2, 2, 32, PAGED, PARTIAL>(args, rows, stream);
+  return launch_attn<D, 4, 1, 64, PAGED, PARTIAL>(args, rows, stream);
+}
+
+template <bool PAGED, bool PARTIAL>
+gqa_status_t dispatch(gqa::AttnArgs args, int d, int64_t rows, hipStream_t stream) {
+  if (d == 64) return dispatch_rows<64, PAGED, PARTIAL>(args, rows, stream);
+  return dispatch_rows<128, PAGED, PARTIAL>(args, rows, stream);
+}
+
+gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int32_t B,
+                          int32_t Hq, int32_t Sq, int32_t d, int32_t n_split, const float* sink,
+                          hipStream_t stream) {
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  if (rows == 0) return GQA_OK;
+  const float2* ml = reinterpret_cast<const float2*>(workspace);
+  const float* ot = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
+                                                   (size_t)rows * n_split * 8);
+  const int64_t nblocks = cdiv(rows, 4);
+  if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  (void)hipGetLastError();
+  if (d == 64)
+    hipLaunchKernelGGL(gqa::merge_kernel<64>, dim3((unsigned)nblocks), dim3(256), 0, stream, ml, ot,
+                       reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq, n_split,
+                       rows);
+  else
+    hipLaunchKernelGGL(gqa::merge_kernel<128>, dim3((unsigned)nblocks), dim3(256), 0, stream, ml,
+                       ot, reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq,
+                       n_split, rows);
+  return check_launch("merge kernel");
+}
+
+gqa::AttnArgs dense_args(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                         const void* v, const int64_t* vs, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t Sq, int32_t Skv, const int32_t* kv_len, float scale,
+                         int32_t causal) {
+  gqa::AttnArgs a{};
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.k = reinterpret_cast<const uint16_t*>(k);
+  a.v = reinterpret_cast<const uint16_t*>(v);
+  a.q_sb = qs[0]; a.q_sh = qs[1]; a.q_ss = qs[2];
+  a.k_sb = ks[0]; a.k_sh = ks[1]; a.k_ss = ks[2];
+  a.v_sb = vs[0]; a.v_sh = vs[1]; a.v_ss = vs[2];
+  a.kv_len = kv_len;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.Sq = Sq; a.Skv = Skv;
+  a.causal = causal;
+  a.tile = 0;
+  a.n_split = 1;
+  a.scale_log2 = scale * gqa::kLog2e;
+  return a;
+}
+
+// Shared checks of the dense entry points.
+gqa_status_t check_dense(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                         const void* v, const int64_t* vs, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t Sq, int32_t Skv, int32_t d, float scale, int32_t causal) {
+  if (B < 0 || Sq < 0 || Skv < 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "B, Sq and Skv must be >= 0");
+  GQA_TRY(check_heads(Hq, Hkv, d));
+  GQA_TRY(check_ptr("q", q));
+  GQA_TRY(check_ptr("k", k));
+  GQA_TRY(check_ptr("v", v));
+  GQA_TRY(check_strides("q", qs, 3));
+  GQA_TRY(check_strides("k", ks, 3));
+  GQA_TRY(check_strides("v", vs, 3));
+  GQA_TRY(check_scale(scale));
+  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  return GQA_OK;
+}
+
+gqa_status_t check_tile(int32_t tile, bool required) {
+  if (tile < 0 || tile % 64 != 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "tile_s_kv (%d) must be 0 or a positive multiple of 64", tile);
+  if (required && tile == 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "tile_s_kv must be a positive multiple of 64");
+  return GQA_OK;
+}
+
+gqa_status_t check_workspace(const void* ws, size_t have, size_t need) {
+  if (need == 0) return GQA_OK;
+  if (!ws) return fail(GQA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(GQA_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+  if (have < need)
+    return fail(GQA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return GQA_OK;
+}
+
+// The partial phase (validated arguments).
+gqa_status_t run_partial(gqa::AttnArgs a, int32_t d, int32_t tile, void* ws, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  const int64_t n_split = a.Skv > 0 ? cdiv(a.Skv, tile) : 1;
+  a.tile = tile;
+  a.n_split = (int32_t)n_split;
+  a.ws_ml = reinterpret_cast<float2*>(ws);
+  a.ws_o = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (size_t)rows * n_split * 8);
+  return dispatch<false, true>(a, d, (int64_t)a.Sq * a.G, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+const char* gqa_last_error(void) { return g_err; }
+
+gqa_status_t gqa_attention_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv,
+                                          int64_t d, int32_t tile_s_kv, size_t* bytes) {
+  if (!bytes) return fail(GQA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (B < 0 || Hq < 0 || Sq < 0 || Skv < 0 || d < 0 || tile_s_kv < 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "negative size");
+  if (tile_s_kv == 0) {
+    *bytes = 0;
+    return ok();
+  }
+  const int64_t n_split = Skv > 0 ? cdiv(Skv, tile_s_kv) : 1;
+  *bytes = workspace_bytes_for(B * Hq * Sq, n_split, d);
+  return ok();
+}
+
+gqa_status_t gqa_attention_prefill(const void* q, const int64_t q_stride[3], const void* k,
+                                   const int64_t k_stride[3], const void* v,
+                                   const int64_t v_stride[3], void* o, const int64_t o_stride[3],
+                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv,
+                                   int32_t d, const int32_t* kv_len, float scale,
+                                   const float* sink, int32_t causal, int32_t tile_s_kv,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  GQA_TRY(check_dense(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv, d, scale, causal));
+  GQA_TRY(check_ptr("o", o));
+  GQA_TRY(check_strides("o", o_stride, 3));
+  GQA_TRY(check_tile(tile_s_kv, false));
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  size_t need = 0;
+  if (tile_s_kv > 0)
+    need = workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d);
+  GQA_TRY(check_workspace(workspace, workspace_bytes, need));
+  if (rows == 0) return ok();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  gqa::AttnArgs a = dense_args(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv,
+                               kv_len, scale, causal);
+  if (tile_s_kv == 0) {
+    a.o = reinterpret_cast<uint16_t*>(o);
+    a.o_sb = o_stride[0]; a.o_sh = o_stride[1]; a.o_ss = o_stride[2];
+    a.sink = sink;
+    GQA_TRY(dispatch<false, false>(a, d, (int64_t)Sq * a.G, st));
+    return ok();
+  }
+  GQA_TRY(run_partial(a, d, tile_s_kv, workspace, st));
+  GQA_TRY(launch_merge(workspace, o, o_stride, B, Hq, Sq, d, a.Skv > 0 ? (int32_t)cdiv(Skv, tile_s_kv) : 1,
+                       sink, st));
+  return ok();
+}
+
+gqa_status_t gqa_attention_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k,
+                                          const int64_t k_stride[3], const void* v,
+                                          const int64_t v_stride[3], void* o,
+                                          const int64_t o_stride[3], int32_t B, int32_t Hq,
+                                          int32_t Hkv, int32_t Skv, int32_t d,
+                                          const int32_t* kv_len, float scale, const float* sink,
+                                          int32_t tile_s_kv, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  GQA_TRY(check_tile(tile_s_kv, true));
+  return gqa_attention_prefill(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, 1,
+                               Skv, d, kv_len, scale, sink, 0, tile_s_kv, workspace,
+                               workspace_bytes, stream);
+}
+
+gqa_status_t gqa_attention_splitkv_partial(const void* q, const int64_t q_stride[3],
+                                           const void* k, const int64_t k_stride[3],
+                                           const void* v, const int64_t v_stride[3], int32_t B,
+                                           int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv,
+                                           int32_t d, const int32_t* kv_len, float scale,
+                                           int32_t causal, int32_t tile_s_kv, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  GQA_TRY(check_dense(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv, d, scale, causal));
+  GQA_TRY(check_tile(tile_s_kv, true));
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  const size_t need = workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d);
+  GQA_TRY(check_workspace(workspace, workspace_bytes, need));
+  if (rows == 0) return ok();
+  gqa::AttnArgs a = dense_args(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv,
+                               kv_len, scale, causal);
+  GQA_TRY(run_partial(a, d, tile_s_kv, workspace, reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+gqa_status_t gqa_attention_splitkv_merge(const void* workspace, size_t workspace_bytes, void* o,
+                                         const int64_t o_stride[3], int32_t B, int32_t Hq,
+                                         int32_t Sq, int32_t d, int32_t n_split,
+                                         const float* sink, void* stream) {
+  if (B < 0 || Sq < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "B and Sq must be >= 0");
+  if (Hq < 1 || n_split < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "Hq and n_split must be >= 1");
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  GQA_TRY(check_ptr("o", o));
+  GQA_TRY(check_strides("o", o_stride, 3));
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  GQA_TRY(check_workspace(workspace, workspace_bytes, workspace_bytes_for(rows, n_split, d)));
+  if (rows == 0) return ok();
+  GQA_TRY(launch_merge(workspace, o, o_stride, B, Hq, Sq, d, n_split, sink,
+                       reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                                 const int32_t* cu_seqlens_q, const void* k_cache,
+                                 const void* v_cache, int64_t kv_stride_page,
+                                 int64_t kv_stride_row, int64_t kv_stride_h,
+                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                 const int32_t* kv_len, void* o, int64_t o_stride_t,
+                                 int64_t o_stride_h, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t page_size, int32_t total_q, int32_t max_q_len,
+                                 float scale, const float* sink, int32_t causal, void* stream) {
+  if (B < 0 || total_q < 0 || max_q_len < 0 || max_pages_per_seq < 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "B, total_q, max_q_len and max_pages_per_seq must be >= 0");
+  GQA_TRY(check_heads(Hq, Hkv, d));
+  if (page_size != 64) return fail(GQA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", page_size);
+  GQA_TRY(check_ptr("q", q));
+  GQA_TRY(check_ptr("o", o));
+  GQA_TRY(check_ptr("k_cache", k_cache));
+  GQA_TRY(check_ptr("v_cache", v_cache));
+  if (!cu_seqlens_q) return fail(GQA_ERR_INVALID_ARGUMENT, "cu_seqlens_q is NULL");
+  if (!page_table) return fail(GQA_ERR_INVALID_ARGUMENT, "page_table is NULL");
+  if (!kv_len) return fail(GQA_ERR_INVALID_ARGUMENT, "kv_len is NULL (required for paged)");
+  const int64_t qs[2] = {q_stride_t, q_stride_h};
+  const int64_t os[2] = {o_stride_t, o_stride_h};
+  const int64_t kvs[3] = {kv_stride_page, kv_stride_row, kv_stride_h};
+  GQA_TRY(check_strides("q", qs, 2));
+  GQA_TRY(check_strides("o", os, 2));
+  GQA_TRY(check_strides("kv", kvs, 3));
+  GQA_TRY(check_scale(scale));
+  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (B == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if ((int64_t)max_pages_per_seq * page_size > 0x7fffffffLL)
+    return fail(GQA_ERR_UNSUPPORTED, "max_pages_per_seq too large");
+
+  gqa::AttnArgs a{};
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.k = reinterpret_cast<const uint16_t*>(k_cache);
+  a.v = reinterpret_cast<const uint16_t*>(v_cache);
+  a.o = reinterpret_cast<uint16_t*>(o);
+  a.q_ss = q_stride_t; a.q_sh = q_stride_h;
+  a.o_ss = o_stride_t; a.o_sh = o_stride_h;
+  a.k_sh = kv_stride_h; a.v_sh = kv_stride_h;
+  a.kv_sp = kv_stride_page; a.kv_sr = kv_stride_row;
+  a.kv_len = kv_len;
+  a.sink = sink;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.Sq = max_q_len;
+  a.Skv = max_pages_per_seq * page_size;
+  a.causal = causal;
+  a.tile = 0;
+  a.n_split = 1;
+  a.scale_log2 = scale * gqa::kLog2e;
+  GQA_TRY(dispatch<true, false>(a, d, (int64_t)max_q_len * a.G, reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+/*
+ * gqa.h -- C ABI of libgqa.so: grouped-query attention forward on AMD MI355X
+ * (CDNA4, gfx950).
+ *
+ *   O = softmax(scale * Q K^T + mask [+ sink]) V
+ *
+ * Hq query heads share Hkv = Hq / G key/value heads; query head h reads
+ * kv head h / G (consecutive groups).  Inputs and output are bf16,
+ * accumulation is fp32.  Sources for the operation's definition:
+ *
+ *  - AstrAI commit log (gitea, ViperEkura/AstrAI): the commit that packs
+ *    HB = min(G, warps) query heads per block so each K/V tile streams once
+ *    per block; the AttentionParams commits (per-dimension strides, NULL
+ *    meaning an optional path is off, q-head/kv-head divisibility and
+ *    head-dim contiguity checks, split-KV scratch validated at the binding);
+ *    the paged-KV commits (KVSource contiguous vs paged, int32 page tables).
+ *  - nvfp4-megamoe-kernel commit log (dsv4/kernels/attention): the commit
+ *    that passes the true kv length apart from the padded one; the sink-bias
+ *    commit (sink already in the scaled domain); the zero-initialised-P
+ *    commit; the multi-tile FA2 and normalise-once commits; the T-stride
+ *    commit (query-row stride distinct from head stride); the pure C API +
+ *    ctypes loader commits; the single-launch batched decode commit.
+ *  - kernbench2 commit log (src/kernbench/benches): the tile-granular
+ *    ring-KV and tile-sweep commits (persistent (m, l, O) merged tile by
+ *    tile, TILE_S_KV = 1024) and the 2-D mesh all-reduce-mlo commit (the
+ *    merge is associative).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers; bf16 tensors are raw 16-bit
+ *    bfloat16 values.  Strides are in ELEMENTS; the head-dim stride is 1.
+ *  - Dense layout: Q/O [B, Hq, Sq, d], K/V [B, Hkv, Skv, d] addressed by the
+ *    (b, h, s) strides passed in `*_stride[3]` (host arrays).
+ *  - kv_len: device int32 [B] giving each sequence's true key count, or NULL
+ *    meaning Skv for every sequence.  Keys at or past kv_len[b] are never read
+ *    into the max, the sum or P.V (padding may hold anything, NaN included).
+ *    Values outside [0, Skv] are clamped on the device.
+ *  - sink: device fp32 [Hq] of per-head sink logits already in the scaled
+ *    domain (an extra softmax column with no value row: it enters the max
+ *    and the denominator, is never multiplied by scale), or NULL for none.
+ *  - causal: 0 or 1.  Causal masking is aligned bottom-right: query row i of
+ *    a sequence with q_len rows and n keys sees keys j <= n - q_len + i.
+ *    With q_len == n this is "row i sees keys 0..i".
+ *  - A row that sees no key and has no sink gets O = 0.
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream).
+ *  - Base pointers must be 16-byte aligned and the (b, h, s) strides of
+ *    bf16 tensors multiples of 8 elements, else GQA_ERR_UNSUPPORTED.
+ *    d must be 64 or 128, else GQA_ERR_UNSUPPORTED.
+ *
+ * Ownership: the caller owns all memory and keeps it alive until the work
+ * enqueued on `stream` completes.  The library never allocates, frees,
+ * synchronises or reads device memory from the host, keeps no pointer after
+ * returning, and is reentrant.  Launches are asynchronous.
+ *
+ * Errors: every function returns a gqa_status_t.  All validation happens
+ * before anything is enqueued: on any status other than GQA_OK or
+ * GQA_ERR_HIP, nothing was launched and O/workspace are untouched.
+ * GQA_ERR_HIP reports a failed launch; for two-kernel calls the first
+ * kernel may already be enqueued.  gqa_last_error() gives a message for
+ * the last failing call on the calling thread.  Nothing aborts, prints or
+ * throws across this boundary.
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+
+typedef int32_t gqa_status_t;
+
+#define GQA_OK 0
+#define GQA_ERR_INVALID_ARGUMENT 1 /* NULL required pointer, bad dims, Hq % Hkv != 0, bad flag */
+#define GQA_ERR_UNSUPPORTED 2      /* d not 64/128, misaligned pointer or stride, page_size != 64 */
+#define GQA_ERR_WORKSPACE 3        /* workspace NULL or smaller than gqa_attention_workspace_size */
+#define GQA_ERR_HIP 4              /* a HIP launch failed; message from hipGetErrorString */
+
+/* GQA_ABI_VERSION of the built library. */
+int32_t gqa_abi_version(void);
+
+/* Thread-local message of the last failing call on this thread ("" if none).
+ * Valid until the next gqa_* call on the same thread. */
+const char* gqa_last_error(void);
+
+/*
+ * Bytes of split-KV workspace for B*Hq*Sq query rows over Skv keys split in
+ * tiles of tile_s_kv keys: n_split = ceil(Skv / tile_s_kv) partial states
+ * (m, l, O~) per row, each (d + 2) fp32 values, rounded up to 256 bytes.
+ * Writes 0 when tile_s_kv == 0 (one pass needs no workspace).
+ *
+ * Workspace layout (also the input of gqa_attention_splitkv_merge), with
+ * rows r = (b * Hq + h) * Sq + i:
+ *   ml[r][s]    : float2 {m_s, l_s}         at byte 0
+ *   ot[r][s][d] : float  O~_s (un-normalised) at byte 8 * rows * n_split
+ * m_s is the split's max of scale*q.k (natural-log domain; -inf when the
+ * split holds no visible key), l_s = sum_j exp(s_j - m_s), O~_s =
+ * sum_j exp(s_j - m_s) v_j (nvfp4-megamoe-kernel commit log, multi-tile FA2
+ * commit: P stays un-normalised; kernbench2 benches commit log, tile-granular
+ * ring-KV commit: the persistent (m, l, O) state).
+ */
+gqa_status_t gqa_attention_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv,
+                                          int64_t d, int32_t tile_s_kv, size_t* bytes);
+
+/*
+ * Dense prefill (any Sq >= 1), one query row per (b, h, i).
+ *  tile_s_kv == 0 : one pass, one kernel; workspace may be NULL.
+ *  tile_s_kv  > 0 : split-KV -- keys cut into tiles of tile_s_kv (a multiple
+ *                   of 64), one partial state per tile and row, then a merge
+ *                   kernel; needs the workspace above.  Same result up to
+ *                   rounding (the merge is associative; a single tile equals
+ *                   one pass -- kernbench2 benches commit log, tile sweep).
+ */
+gqa_status_t gqa_attention_prefill(const void* q, const int64_t q_stride[3],
+                                   const void* k, const int64_t k_stride[3],
+                                   const void* v, const int64_t v_stride[3],
+                                   void* o, const int64_t o_stride[3],
+                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Skv,
+                                   int32_t d, const int32_t* kv_len, float scale,
+                                   const float* sink, int32_t causal, int32_t tile_s_kv,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Single-token decode with split-KV (Sq = 1 implied; causal is a no-op for
+ * one trailing query).  tile_s_kv must be a positive multiple of 64
+ * (1024 is the pages' TILE_S_KV).  Launches the partial kernel, then the
+ * merge kernel, on `stream`.  Q/O strides as for prefill (the s stride is
+ * unused but must still be a multiple of 8).
+ */
+gqa_status_t gqa_attention_decode_splitkv(const void* q, const int64_t q_stride[3],
+                                          const void* k, const int64_t k_stride[3],
+                                          const void* v, const int64_t v_stride[3],
+                                          void* o, const int64_t o_stride[3],
+                                          int32_t B, int32_t Hq, int32_t Hkv, int32_t Skv,
+                                          int32_t d, const int32_t* kv_len, float scale,
+                                          const float* sink, int32_t tile_s_kv,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two phases of split-KV on their own, for callers that place the
+ * partial states themselves (for instance KV sharded across devices, with
+ * the partials gathered before one merge; the merge is associative -- see
+ * the kernbench2 2-D mesh all-reduce-mlo commit).
+ *
+ * _partial: writes n_split = ceil(Skv / tile_s_kv) partial states per query
+ *   row into `workspace` (layout above).  The sink is NOT applied here.
+ * _merge:   reads n_split partial states per row from `workspace` and
+ *   writes O = sum_s O~_s e^(m_s - M) / (e^(sink - M) + sum_s l_s e^(m_s - M)),
+ *   M = max(sink, max_s m_s), normalised exactly once, as bf16.  Splits
+ *   with m_s = -inf weigh 0; a row with M = -inf gets 0.
+ */
+gqa_status_t gqa_attention_splitkv_partial(const void* q, const int64_t q_stride[3],
+                                           const void* k, const int64_t k_stride[3],
+                                           const void* v, const int64_t v_stride[3],
+                                           int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq,
+                                           int32_t Skv, int32_t d, const int32_t* kv_len,
+                                           float scale, int32_t causal, int32_t tile_s_kv,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+gqa_status_t gqa_attention_splitkv_merge(const void* workspace, size_t workspace_bytes,
+                                         void* o, const int64_t o_stride[3], int32_t B,
+                                         int32_t Hq, int32_t Sq, int32_t d, int32_t n_split,
+                                         const float* sink, void* stream);
+
+/*
+ * Ragged-Q, paged-KV attention (AstrAI commit log: packed 3-D inference
+ * tensors with a KV cache, int32 page tables, KVSource contiguous vs paged).
+ *
+ *  q / o        : packed bf16 [total_q, Hq, d]; token t of sequence b is row
+ *                 cu_seqlens_q[b] + i, i < q_len_b = cu[b+1] - cu[b].
+ *                 Strides (t, h) in elements.
+ *  cu_seqlens_q : device int32 [B + 1], cu[0] = 0, non-decreasing,
+ *                 every q_len_b <= max_q_len.
+ *  k_cache/v_cache : bf16 page pools; key row j of sequence b lives in page
+ *                 page_table[b * max_pages_per_seq + j / page_size] at in-page
+ *                 row j % page_size, kv head g, addressed as
+ *                 page * kv_stride_page + row * kv_stride_row + g * kv_stride_h.
+ *                 Default layout [n_pages][page_size][Hkv][d].
+ *  page_table   : device int32 [B, max_pages_per_seq]; entries past a
+ *                 sequence's last page are never read.
+ *  kv_len       : device int32 [B], required.
+ *  page_size    : must be 64.
+ *  max_q_len    : host bound on q_len_b that sizes the grid (no device read).
+ * Page ids are trusted: an id outside the pool is undefined behaviour.
+ */
+gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                                 const int32_t* cu_seqlens_q, const void* k_cache,
+                                 const void* v_cache, int64_t kv_stride_page,
+                                 int64_t kv_stride_row, int64_t kv_stride_h,
+                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                 const int32_t* kv_len, void* o, int64_t o_stride_t,
+                                 int64_t o_stride_h, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t d, int32_t page_size, int32_t total_q,
+                                 int32_t max_q_len, float scale, const float* sink,
+                                 int32_t causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

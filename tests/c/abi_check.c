@@ -1,0 +1,83 @@
+/* Pure-C check of libgqa's boundary: every validation error is returned
+ * before anything touches a device, so this runs on a machine with no GPU.
+ * Pointers here are fake host addresses that are never dereferenced. */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gqa.h"
+
+static int failures = 0;
+
+static void expect(const char* what, gqa_status_t got, gqa_status_t want) {
+  if (got != want) {
+    printf("FAIL %s: got %d want %d (%s)\n", what, got, want, gqa_last_error());
+    ++failures;
+  } else {
+    printf("ok   %s -> %d (%s)\n", what, got, gqa_last_error());
+  }
+}
+
+int main(void) {
+  void* P = (void*)(uintptr_t)0x10000;  /* aligned, never dereferenced */
+  void* M = (void*)(uintptr_t)0x10002;  /* misaligned */
+  const int64_t s[3] = {4096, 1024, 64};
+  const int64_t bad[3] = {4096, 1024, 60};
+  size_t ws = 0;
+
+  if (gqa_abi_version() != GQA_ABI_VERSION) { printf("FAIL abi version\n"); ++failures; }
+  expect("workspace size", gqa_attention_workspace_size(16, 32, 1, 8192, 128, 1024, &ws), GQA_OK);
+  if (ws != (size_t)16 * 32 * 8 * 130 * 4) { printf("FAIL workspace bytes %zu\n", ws); ++failures; }
+  expect("workspace size tile 0", gqa_attention_workspace_size(1, 1, 1, 1, 64, 0, &ws), GQA_OK);
+  if (ws != 0) { printf("FAIL tile-0 workspace %zu\n", ws); ++failures; }
+  expect("workspace size NULL out", gqa_attention_workspace_size(1, 1, 1, 1, 64, 64, NULL),
+         GQA_ERR_INVALID_ARGUMENT);
+
+#define PREFILL(q, qs, d, hq, hkv, scale, causal, tile, w, wb) \
+  gqa_attention_prefill(q, qs, P, s, P, s, P, s, 1, hq, hkv, 16, 128, d, NULL, scale, NULL, \
+                        causal, tile, w, wb, NULL)
+  expect("NULL q", PREFILL(NULL, s, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("misaligned q", PREFILL(M, s, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
+  expect("stride not x8", PREFILL(P, bad, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
+  expect("NULL strides", PREFILL(P, NULL, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("d = 96", PREFILL(P, s, 96, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
+  expect("Hq % Hkv", PREFILL(P, s, 64, 6, 4, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("Hkv = 0", PREFILL(P, s, 64, 4, 0, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("scale 0", PREFILL(P, s, 64, 4, 1, 0.0f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("scale nan", PREFILL(P, s, 64, 4, 1, NAN, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("causal 2", PREFILL(P, s, 64, 4, 1, 0.125f, 2, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("tile 100", PREFILL(P, s, 64, 4, 1, 0.125f, 0, 100, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("split, no workspace", PREFILL(P, s, 64, 4, 1, 0.125f, 0, 64, NULL, 0), GQA_ERR_WORKSPACE);
+  expect("split, small workspace", PREFILL(P, s, 64, 4, 1, 0.125f, 0, 64, P, 1024), GQA_ERR_WORKSPACE);
+  expect("split, misaligned workspace", PREFILL(P, s, 64, 4, 1, 0.125f, 0, 64, M, 1 << 20),
+         GQA_ERR_WORKSPACE);
+  expect("negative B",
+         gqa_attention_prefill(P, s, P, s, P, s, P, s, -1, 4, 1, 16, 128, 64, NULL, 0.125f, NULL,
+                               0, 0, NULL, 0, NULL), GQA_ERR_INVALID_ARGUMENT);
+  expect("decode tile 0",
+         gqa_attention_decode_splitkv(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,
+                                      0.088f, NULL, 0, P, 1 << 30, NULL), GQA_ERR_INVALID_ARGUMENT);
+  expect("decode no workspace",
+         gqa_attention_decode_splitkv(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,
+                                      0.088f, NULL, 1024, NULL, 0, NULL), GQA_ERR_WORKSPACE);
+  expect("partial no workspace",
+         gqa_attention_splitkv_partial(P, s, P, s, P, s, 2, 8, 2, 3, 300, 64, NULL, 0.125f, 0, 64,
+                                       NULL, 0, NULL), GQA_ERR_WORKSPACE);
+  expect("merge small workspace",
+         gqa_attention_splitkv_merge(P, 256, P, s, 2, 8, 3, 64, 5, NULL, NULL), GQA_ERR_WORKSPACE);
+  expect("merge n_split 0",
+         gqa_attention_splitkv_merge(P, 1 << 20, P, s, 2, 8, 3, 64, 0, NULL, NULL),
+         GQA_ERR_INVALID_ARGUMENT);
+#define PAGED(cu, pt, kvl, page, d, causal) \
+  gqa_attention_paged(P, 4096, 128, cu, P, P, 8192, 128, 128, pt, 64, kvl, P, 4096, 128, 8, 32, \
+                      1, d, page, 100, 64, 0.088f, NULL, causal, NULL)
+  expect("paged page 32", PAGED(P, P, P, 32, 128, 0), GQA_ERR_UNSUPPORTED);
+  expect("paged NULL cu", PAGED(NULL, P, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("paged NULL table", PAGED(P, NULL, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("paged NULL kv_len", PAGED(P, P, NULL, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
+  expect("paged d 256", PAGED(P, P, P, 64, 256, 0), GQA_ERR_UNSUPPORTED);
+  expect("paged causal 3", PAGED(P, P, P, 64, 128, 3), GQA_ERR_INVALID_ARGUMENT);
+  printf("%s\n", failures ? "FAILED" : "ALL OK");
+  return failures ? 1 : 0;
+}

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerance (over valid output positions, every d): max-abs 1e-2 and mean-abs
+1e-3 against the oracle on the same bf16 inputs.  Where the result is fixed
+exactly (one visible key, an all-masked row), the test is bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import to_f64
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+
+
+def gqa():
+    import gqa_attention_forward_amd as m
+    return m
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def assert_close(got, want, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - want)
+    mx, mean = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    print(f"  {what}: max_abs={mx:.3e} mean_abs={mean:.3e} max|O|={np.abs(want).max(initial=0):.3f}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{what}: max {mx} mean {mean}"
+
+
+def to_dev(inp):
+    d = dev()
+    return {k: (v.to(d) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def run_dense(inp, *, causal=False, tile=0, use_sink=True, decode=False):
+    g = to_dev(inp)
+    kw = dict(kv_len=g["kv_len"], scale=inp["scale"], sink=g["sink"] if use_sink else None)
+    if decode:
+        out = gqa().decode_splitkv(g["q"], g["k"], g["v"], tile_s_kv=tile, **kw)
+    else:
+        out = gqa().prefill(g["q"], g["k"], g["v"], causal=causal, tile_s_kv=tile, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def oracle_dense(inp, *, causal=False, use_sink=True):
+    kvl = None if inp["kv_len"] is None else inp["kv_len"].numpy()
+    snk = to_f64(inp["sink"]) if use_sink else None
+    return oracle.attention_fp64(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]),
+                                 scale=inp["scale"], kv_len=kvl, sink=snk, causal=causal)
+
+
+# ---------------------------------------------------------------- named workloads
+
+def test_tiny_prefill_full():
+    c = workloads.CASES["tiny_prefill"]
+    note(f"tiny_prefill {c}")
+    inp = workloads.make_case(c)
+    assert_close(run_dense(inp), oracle_dense(inp), "tiny_prefill")
+
+
+def _sampled_rows(inp, out, rows, causal):
+    q, k, v = inp["q"], inp["k"].float().numpy(), inp["v"].float().numpy()
+    b, h, i = rows
+    want = oracle.attention_rows_fp64(q.float().numpy(), k, v, b, h, i, scale=inp["scale"],
+                                      kv_len=inp["kv_len"].numpy(), causal=causal)
+    return out[b, h, i], want
+
+
+def _rows(c, n, seed):
+    r = np.random.default_rng(seed)
+    b = r.integers(0, c.B, n)
+    h = r.integers(0, c.Hq, n)
+    i = r.integers(0, c.Sq, n)
+    i[:4] = [0, c.Sq - 1, c.Sq // 2, max(0, c.Sq - 2)]  # include the edges
+    return b, h, i
+
+
+@pytest.mark.parametrize("name", ["decode_splitkv", "shortq_longkv", "causal_prefill"])
+def test_full_size_sampled(name):
+    c = workloads.CASES[name]
+    note(f"{name} full size {c}")
+    inp = workloads.make_case(c)
+    tile = c.tile_s_kv if c.decode else (2048 if name == "shortq_longkv" else 0)
+    out = run_dense(inp, causal=c.causal, tile=tile, use_sink=False, decode=c.decode)
+    assert out.shape == (c.B, c.Hq, c.Sq, c.d)
+    assert np.all(np.isfinite(out))
+    got, want = _sampled_rows(inp, out, _rows(c, 160, 7), c.causal)
+    assert_close(got, want, name)
+
+
+def test_shortq_longkv_one_pass_equals_split():
+    c = workloads.CASES["shortq_longkv"]
+    inp = workloads.make_case(c)
+    note("shortq_longkv one pass vs split 2048")
+    a = run_dense(inp, tile=0, use_sink=False)
+    b = run_dense(inp, tile=2048, use_sink=False)
+    assert np.abs(a - b).max() <= 2 * 2.0 ** -8 * np.abs(a).max() + 1e-6
+
+
+def test_ragged_paged_full():
+    note("ragged paged workload (B=8, Hq=32, Hkv=1, NaN padding, sink)")
+    w = workloads.make_paged()
+    g = to_dev(w)
+    out = gqa().paged(g["q"], g["cu_seqlens_q"], g["k_cache"], g["v_cache"], g["page_table"],
+                      g["kv_len"], max_q_len=w["max_q_len"], scale=w["scale"], sink=g["sink"])
+    torch.cuda.synchronize()
+    want = oracle.paged_attention_fp64(to_f64(w["q"]), w["cu_seqlens_q"].numpy(),
+                                       to_f64(w["k_cache"]), to_f64(w["v_cache"]),
+                                       w["page_table"].numpy(), w["kv_len"].numpy(),
+                                       scale=w["scale"], page_size=64, sink=to_f64(w["sink"]))
+    assert_close(out.float().cpu().numpy(), want, "paged")
+
+
+# ---------------------------------------------------------------- small sweeps
+
+SWEEP = [
+    # B, Hq, Hkv, Sq, Skv, d
+    (2, 8, 2, 37, 301, 128),
+    (2, 8, 2, 37, 301, 64),
+    (1, 32, 4, 16, 700, 128),
+    (3, 4, 4, 5, 129, 128),
+    (2, 12, 3, 70, 70, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SWEEP)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tile", [0, 64, 192])
+def test_sweep(shape, causal, tile):
+    B, Hq, Hkv, Sq, Skv, d = shape
+    note(f"sweep {shape} causal={causal} tile={tile}")
+    inp = workloads.make_dense(B, Hq, Hkv, Sq, Skv, d, seed=hash((shape, causal)) % 10000,
+                               kv_len="random", sink=True, nan_pad=True)
+    got = run_dense(inp, causal=causal, tile=tile)
+    want = oracle_dense(inp, causal=causal)
+    assert_close(got, want, f"{shape} c={causal} t={tile}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 32])
+def test_group_sizes(G):
+    """The pages' SDPA-checked group sizes (AstrAI commit log, HB packing commit)."""
+    Hkv = 2 if G <= 8 else 1
+    note(f"group size G={G}")
+    for Sq in (1, 9, 64):
+        inp = workloads.make_dense(2, Hkv * G, Hkv, Sq, 200, 128, seed=50 + G + Sq,
+                                   kv_len="random", sink=G % 2 == 0, nan_pad=True)
+        got = run_dense(inp, causal=Sq > 1)
+        want = oracle_dense(inp, causal=Sq > 1)
+        assert_close(got, want, f"G={G} Sq={Sq}")
+
+
+@pytest.mark.parametrize("Skv", [1, 63, 1024, 3000])
+def test_decode_sweep(Skv):
+    note(f"decode Skv={Skv}")
+    inp = workloads.make_dense(4, 32, 8, 1, Skv, 128, seed=Skv, kv_len="random", sink=True,
+                               nan_pad=True)
+    got = run_dense(inp, tile=1024, decode=True)
+    assert_close(got, oracle_dense(inp), f"decode Skv={Skv}")
+
+
+# ---------------------------------------------------------------- invariants and edges
+
+def test_kvlen_one_is_exact_v0():
+    """One valid key among 128 padded (NaN) rows: O is that V row, bit for bit."""
+    note("kv_len = 1, Skv = 128 NaN padded")
+    inp = workloads.make_dense(2, 8, 2, 16, 128, 128, seed=3, kv_len=[1, 1], nan_pad=True)
+    for tile in (0, 64):
+        out = run_dense(inp, tile=tile, use_sink=False)
+        v0 = inp["v"][:, :, :1].float().numpy()
+        want = np.repeat(v0, 4, axis=1)
+        np.testing.assert_array_equal(out, np.broadcast_to(want, out.shape))
+
+
+def test_empty_rows_are_zero_and_sink_neg_inf_is_no_sink():
+    note("kv_len = 0 rows, causal rows with no key, sink = -inf")
+    inp = workloads.make_dense(2, 4, 1, 6, 64, 64, seed=4, kv_len=[0, 3], nan_pad=True)
+    out = run_dense(inp, use_sink=False)
+    assert np.all(out[0] == 0)
+    outc = run_dense(inp, causal=True, use_sink=False)
+    assert np.all(outc[1, :, :3] == 0)          # rows 0..2 see no key (bottom-right)
+    assert_close(outc, oracle_dense(inp, causal=True, use_sink=False), "causal empty rows")
+    inp2 = dict(inp, sink=torch.full((4,), -math.inf), kv_len=torch.tensor([64, 5], dtype=torch.int32))
+    inp2["k"] = inp["k"].nan_to_num()
+    inp2["v"] = inp["v"].nan_to_num()
+    a = run_dense(inp2, use_sink=True)
+    b = run_dense(inp2, use_sink=False)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_decode_equals_last_prefill_row():
+    note("decode vs last row of causal prefill")
+    inp = workloads.make_dense(2, 16, 4, 40, 300, 128, seed=5, kv_len=[300, 211], sink=True,
+                               nan_pad=True)
+    pre = run_dense(inp, causal=True)
+    dec_inp = dict(inp, q=inp["q"][:, :, -1:].contiguous())
+    dec = run_dense(dec_inp, tile=128, decode=True)
+    assert np.abs(pre[:, :, -1] - dec[:, :, 0]).max() <= 4e-3
+
+
+def test_strided_views():
+    """(B, S, H, d) storage seen as [B, H, S, d]: distinct s and h strides."""
+    note("strided q/k/v/o views")
+    B, Hq, Hkv, S, d = 2, 8, 2, 33, 128
+    base = workloads.make_dense(B, Hq, Hkv, S, S, d, seed=6, sink=True)
+    D = dev()
+    q = base["q"].transpose(1, 2).contiguous().to(D).transpose(1, 2)
+    k = base["k"].transpose(1, 2).contiguous().to(D).transpose(1, 2)
+    v = base["v"].transpose(1, 2).contiguous().to(D).transpose(1, 2)
+    out = torch.empty(B, S, Hq, d, dtype=torch.bfloat16, device=D).transpose(1, 2)
+    gqa().prefill(q, k, v, scale=base["scale"], sink=base["sink"].to(D), causal=True, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().numpy(), oracle_dense(base, causal=True), "strided")
+
+
+def test_partial_states_match_oracle():
+    note("split-KV partial states vs oracle partials")
+    inp = workloads.make_dense(2, 8, 2, 3, 300, 128, seed=8, kv_len=[300, 100])
+    g = to_dev(inp)
+    ml, ot, ws = gqa().splitkv_partial(g["q"], g["k"], g["v"], tile_s_kv=128, kv_len=g["kv_len"],
+                                       scale=inp["scale"], causal=True)
+    torch.cuda.synchronize()
+    m, l, o = oracle.splitkv_partials_fp64(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]),
+                                           scale=inp["scale"], tile=128,
+                                           kv_len=inp["kv_len"].numpy(), causal=True)
+    ns = m.shape[-1]
+    ml = ml.cpu().numpy().reshape(2, 8, 3, ns, 2)
+    ot = ot.cpu().numpy().reshape(2, 8, 3, ns, 128)
+    live = m > -np.inf
+    assert np.array_equal(ml[..., 0] > -np.inf, live)
+    assert np.all(ml[..., 1][~live] == 0) and np.all(ot[~live] == 0)
+    # compare normalised partials (each one's softmax over its own split)
+    np.testing.assert_allclose(ml[..., 0][live], m[live], rtol=1e-5, atol=1e-5)
+    rel = ot[live] / ml[..., 1][live][:, None] - o[live] / l[live][:, None]
+    assert np.abs(rel).max() <= MAX_ABS
+    out = gqa().splitkv_merge(ws, B=2, Hq=8, Sq=3, d=128, n_split=ns)
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().numpy(), oracle_dense(inp, causal=True, use_sink=False), "merge")
+
+
+def test_repeat_runs_bit_identical():
+    note("repeated launches are bit-identical")
+    inp = workloads.make_dense(2, 32, 8, 64, 1000, 128, seed=9, kv_len="random", sink=True,
+                               nan_pad=True)
+    g = to_dev(inp)
+    ref = gqa().prefill(g["q"], g["k"], g["v"], kv_len=g["kv_len"], sink=g["sink"], causal=True)
+    for _ in range(20):
+        again = gqa().prefill(g["q"], g["k"], g["v"], kv_len=g["kv_len"], sink=g["sink"],
+                              causal=True)
+        assert torch.equal(ref.view(torch.int16), again.view(torch.int16))
+
+
+def test_empty_batch_is_noop():
+    note("B = 0")
+    D = dev()
+    q = torch.empty(0, 4, 3, 64, dtype=torch.bfloat16, device=D)
+    k = torch.empty(0, 1, 5, 64, dtype=torch.bfloat16, device=D)
+    out = gqa().prefill(q, k, k)
+    assert out.shape == q.shape

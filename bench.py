@@ -208,7 +208,9 @@ def bench_secondary(args, device, stream):
 
 
 def cpu_baseline(inp, c, budget_s):
-    """The oracle on this host's cores over whole decode sequences until ~budget_s."""
+    """The oracle on this host's cores, cycling over whole decode sequences
+    (all heads and keys of one sequence per call) until ~budget_s seconds of
+    oracle time; fp64 input conversion is outside the timed region."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -216,12 +218,13 @@ def cpu_baseline(inp, c, budget_s):
     except Exception:  # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
     elapsed, done = 0.0, 0
-    q = inp["q"]
-    k, v = inp["k"], inp["v"]
-    while done < c.B and elapsed < budget_s:
-        qb = q[done:done + 1].to(torch.float64).numpy()
-        kb = k[done:done + 1].to(torch.float64).numpy()
-        vb = v[done:done + 1].to(torch.float64).numpy()
+    cache = {}
+    while elapsed < budget_s:
+        b = done % c.B
+        if b not in cache:
+            cache[b] = tuple(t[b:b + 1].to(torch.float64).numpy()
+                             for t in (inp["q"], inp["k"], inp["v"]))
+        qb, kb, vb = cache[b]
         t0 = time.perf_counter()
         oracle.attention_fp64(qb, kb, vb, scale=inp["scale"])
         elapsed += time.perf_counter() - t0
@@ -229,8 +232,8 @@ def cpu_baseline(inp, c, budget_s):
     per_seq = (2 * c.Hq * c.d * 2) + 2 * c.Hkv * c.Skv * c.d * 2
     return {"value": round(done * per_seq / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} of {c.B} decode sequences (all {c.Hq} heads x {c.Skv} keys each), "
-                      f"{elapsed:.1f} s of oracle time"}
+            "sample": f"{done} decode sequences of the decode_splitkv workload (cycling over its "
+                      f"{c.B}; each all {c.Hq} heads x {c.Skv} keys), {elapsed:.1f} s of oracle time"}
 
 
 def main():

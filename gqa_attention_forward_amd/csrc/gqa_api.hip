@@ -175,14 +175,15 @@ gqa_status_t check_dense(const void* q, const int64_t* qs, const void* k, const 
   if (B < 0 || Sq < 0 || Skv < 0)
     return fail(GQA_ERR_INVALID_ARGUMENT, "B, Sq and Skv must be >= 0");
   GQA_TRY(check_heads(Hq, Hkv, d));
+  GQA_TRY(check_scale(scale));
+  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if ((int64_t)B * Sq == 0) return GQA_OK;  // empty: nothing is read or written
   GQA_TRY(check_ptr("q", q));
   GQA_TRY(check_ptr("k", k));
   GQA_TRY(check_ptr("v", v));
   GQA_TRY(check_strides("q", qs, 3));
   GQA_TRY(check_strides("k", ks, 3));
   GQA_TRY(check_strides("v", vs, 3));
-  GQA_TRY(check_scale(scale));
-  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   return GQA_OK;
 }
 
@@ -244,10 +245,11 @@ gqa_status_t gqa_attention_prefill(const void* q, const int64_t q_stride[3], con
                                    const float* sink, int32_t causal, int32_t tile_s_kv,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   GQA_TRY(check_dense(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv, d, scale, causal));
-  GQA_TRY(check_ptr("o", o));
-  GQA_TRY(check_strides("o", o_stride, 3));
   GQA_TRY(check_tile(tile_s_kv, false));
   const int64_t rows = (int64_t)B * Hq * Sq;
+  if (rows == 0) return ok();
+  GQA_TRY(check_ptr("o", o));
+  GQA_TRY(check_strides("o", o_stride, 3));
   size_t need = 0;
   if (tile_s_kv > 0)
     need = workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d);
@@ -293,6 +295,7 @@ gqa_status_t gqa_attention_splitkv_partial(const void* q, const int64_t q_stride
   GQA_TRY(check_dense(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv, d, scale, causal));
   GQA_TRY(check_tile(tile_s_kv, true));
   const int64_t rows = (int64_t)B * Hq * Sq;
+  if (rows == 0) return ok();
   const size_t need = workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d);
   GQA_TRY(check_workspace(workspace, workspace_bytes, need));
   if (rows == 0) return ok();
@@ -309,11 +312,11 @@ gqa_status_t gqa_attention_splitkv_merge(const void* workspace, size_t workspace
   if (B < 0 || Sq < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "B and Sq must be >= 0");
   if (Hq < 1 || n_split < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "Hq and n_split must be >= 1");
   if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  if (rows == 0) return ok();
   GQA_TRY(check_ptr("o", o));
   GQA_TRY(check_strides("o", o_stride, 3));
-  const int64_t rows = (int64_t)B * Hq * Sq;
   GQA_TRY(check_workspace(workspace, workspace_bytes, workspace_bytes_for(rows, n_split, d)));
-  if (rows == 0) return ok();
   GQA_TRY(launch_merge(workspace, o, o_stride, B, Hq, Sq, d, n_split, sink,
                        reinterpret_cast<hipStream_t>(stream)));
   return ok();
@@ -332,6 +335,9 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
     return fail(GQA_ERR_INVALID_ARGUMENT, "B, total_q, max_q_len and max_pages_per_seq must be >= 0");
   GQA_TRY(check_heads(Hq, Hkv, d));
   if (page_size != 64) return fail(GQA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", page_size);
+  GQA_TRY(check_scale(scale));
+  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (B == 0 || total_q == 0 || max_q_len == 0) return ok();
   GQA_TRY(check_ptr("q", q));
   GQA_TRY(check_ptr("o", o));
   GQA_TRY(check_ptr("k_cache", k_cache));
@@ -345,9 +351,6 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
   GQA_TRY(check_strides("q", qs, 2));
   GQA_TRY(check_strides("o", os, 2));
   GQA_TRY(check_strides("kv", kvs, 3));
-  GQA_TRY(check_scale(scale));
-  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
-  if (B == 0 || total_q == 0 || max_q_len == 0) return ok();
   if ((int64_t)max_pages_per_seq * page_size > 0x7fffffffLL)
     return fail(GQA_ERR_UNSUPPORTED, "max_pages_per_seq too large");
 

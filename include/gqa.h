@@ -43,6 +43,9 @@
  *    With q_len == n this is "row i sees keys 0..i".
  *  - A row that sees no key and has no sink gets O = 0.
  *  - stream: a hipStream_t passed as void* (NULL = the null stream).
+ *  - A call with no output rows (B * Sq == 0; for paged B, total_q or
+ *    max_q_len == 0) is a no-op that returns GQA_OK after the scalar checks;
+ *    its pointers are not examined and may be NULL.
  *  - Base pointers must be 16-byte aligned and the (b, h, s) strides of
  *    bf16 tensors multiples of 8 elements, else GQA_ERR_UNSUPPORTED.
  *    d must be 64 or 128, else GQA_ERR_UNSUPPORTED.

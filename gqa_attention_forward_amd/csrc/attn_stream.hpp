@@ -1,0 +1,354 @@
+// Stream GQA forward kernel for query groups of at most 16 * NQB rows per
+// (b, kv head): single-token decode and short query blocks.
+//
+// Each workgroup owns one (b, kv head g, q-tile, kv split).  Its NW waves
+// split the split's keys into 32-key tiles taken round-robin, and each wave
+// streams its tiles on its own: there is no workgroup barrier inside the key
+// loop.  A wave keeps the next tile's K and V in flight in registers while it
+// computes on the current one.  The waves' running states (m, l, O) are
+// combined through LDS at the end (the associative (m, l, O) merge of the
+// kernbench2 2-D mesh all-reduce-mlo commit), then written as one split
+// partial or as the final normalised output.
+//
+// MFMA mapping, v_mfma_f32_16x16x32_bf16 (16 query columns per block, so a
+// 4-row GQA group wastes 12 columns instead of 28 with the 32-wide form):
+//   S^T[key][q] = K Q^T : A = K straight from global memory (lane = key row
+//                         c16, 8 d per lane group), B = Q in registers.
+//   O^T[d][q] += V^T P^T: B = P from the S^T accumulators of the lane (two
+//                         16-key blocks -> 8 keys), A = V^T read from a
+//                         wave-private row-major LDS tile with
+//                         ds_read_b64_tr_b16 (within each 16-lane group,
+//                         destination lane i, element e comes from source
+//                         lane 4e + i/4, element i%4 -- so each source lane
+//                         points at 4 d of one key row and every lane gets 4
+//                         keys of one d).
+//   16-byte V slots in LDS are XOR-swizzled by (key % (D/8)), which makes
+//   both the b128 row writes and the transposing reads bank-conflict free.
+#pragma once
+
+#include "common.hpp"
+
+namespace gqa {
+
+template <int D, int NQB>
+struct StreamCfg {
+  static constexpr int BK = 32;             // keys per tile
+  static constexpr int NC = D / 32;         // 32-wide d steps of Q.K
+  static constexpr int NDB = D / 16;        // 16-row d blocks of O^T
+  static constexpr int DC = D / 8;          // 16-byte chunks per row
+  static constexpr int VPL = BK * DC / 64;  // V chunks per lane per tile
+  static constexpr int VTILE = BK * D;      // V tile elements (per wave)
+  static constexpr int SLOT_F = NQB * (2 + 4 * NDB) * 64;  // combine floats per wave
+  static constexpr int WAVE_BYTES =
+      (VTILE * 2 > SLOT_F * 4 ? VTILE * 2 : SLOT_F * 4);
+};
+
+// Two waves per SIMD for one 16-column block; one for two blocks (the second
+// block's Q, S and O would not fit two waves' register budget).
+template <int D, int NQB, int NW, bool PAGED, bool PARTIAL>
+__global__ void __launch_bounds__(NW * 64, NQB == 1 ? 2 : 1)
+attn_stream_kernel(const AttnArgs a) {
+  using C = StreamCfg<D, NQB>;
+  constexpr int BK = C::BK;
+  constexpr int NC = C::NC;
+  constexpr int NDB = C::NDB;
+  constexpr int DC = C::DC;
+  constexpr int VPL = C::VPL;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int L = blockIdx.x;
+  const int nbg = a.B * a.Hkv;
+  const int bg = L % nbg;
+  const int rest = L / nbg;
+  const int split = rest % a.n_split;
+  const int qt = a.n_qtiles - 1 - rest / a.n_split;
+  const int b = bg / a.Hkv;
+  const int g = bg % a.Hkv;
+  const int G = a.G;
+
+  int q_len, q_row0 = 0;
+  if constexpr (PAGED) {
+    q_row0 = a.cu_seqlens_q[b];
+    q_len = a.cu_seqlens_q[b + 1] - q_row0;
+  } else {
+    q_len = a.Sq;
+  }
+  int n = a.Skv;
+  if (a.kv_len) n = min(max(a.kv_len[b], 0), a.Skv);
+  const int rows_total = q_len * G;
+  const int row0 = qt * (16 * NQB);
+  if (row0 >= rows_total) return;
+
+  int kbeg = 0, kend = n;
+  if (a.tile > 0) {
+    kbeg = split * a.tile;
+    kend = min(n, kbeg + a.tile);
+  }
+  if (a.causal) {
+    const int p_last = (min(row0 + 16 * NQB, rows_total) - 1) / G;
+    kend = min(kend, min(max(n - q_len + p_last + 1, 0), n));
+  }
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  // below wlo no row of the workgroup is masked
+  int wlo = kend;
+  if (a.causal) wlo = min(kend, min(max(n - q_len + row0 / G + 1, 0), n));
+
+  // ---- this lane's query columns (one per 16-column block)
+  bool rvalid[NQB];
+  int pq[NQB], hq[NQB], lim[NQB];
+  bf16x8 qf[NQB][NC];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int rho = row0 + 16 * qb + c16;
+    rvalid[qb] = rho < rows_total;
+    pq[qb] = rvalid[qb] ? rho / G : 0;
+    hq[qb] = g * G + (rvalid[qb] ? rho - pq[qb] * G : 0);
+    lim[qb] = kend;
+    if (a.causal) lim[qb] = min(kend, min(max(n - q_len + pq[qb] + 1, 0), n));
+    const uint16_t* qp;
+    if constexpr (PAGED)
+      qp = a.q + (int64_t)(q_row0 + pq[qb]) * a.q_ss + (int64_t)hq[qb] * a.q_sh;
+    else
+      qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq[qb] * a.q_sh + (int64_t)pq[qb] * a.q_ss;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qf[qb][c] = rvalid[qb] ? *reinterpret_cast<const bf16x8*>(qp + 32 * c + 8 * grp)
+                             : bf16x8{};
+  }
+
+  float m[NQB], l[NQB];
+  f32x4 acc[NQB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = -INFINITY;
+    if constexpr (!PARTIAL)
+      if (a.sink && rvalid[qb]) m[qb] = a.sink[hq[qb]] * kLog2e;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{};
+  }
+
+  auto krow = [&](int key) -> const uint16_t* {
+    if constexpr (PAGED) {
+      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
+      return a.k + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.k_sh;
+    } else {
+      return a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)key * a.k_ss;
+    }
+  };
+  auto vrow = [&](int key) -> const uint16_t* {
+    if constexpr (PAGED) {
+      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
+      return a.v + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.v_sh;
+    } else {
+      return a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)key * a.v_ss;
+    }
+  };
+
+  // one tile in registers: K in MFMA A layout, V as row chunks.  Keys at or
+  // past kend are never read: their loads are redirected to row kend - 1
+  // (real, finite data) and the keys are masked below, so they get P = 0
+  // exactly.  Branch-free loads keep the compiler's wait counts exact, which
+  // is what lets the next tile's loads stay in flight during this tile's math.
+  struct Tile {
+    uint4 k[2][NC];
+    uint4 v[VPL];
+  };
+  const int klast = kend - 1;
+  auto load = [&](int j0, Tile& t) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint16_t* r = krow(min(j0 + 16 * kb + c16, klast));
+#pragma unroll
+      for (int c = 0; c < NC; ++c) t.k[kb][c] = *reinterpret_cast<const uint4*>(r + 32 * c + 8 * grp);
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int ci = lane + 64 * j;
+      t.v[j] = *reinterpret_cast<const uint4*>(vrow(min(j0 + ci / DC, klast)) + 8 * (ci % DC));
+    }
+  };
+
+  uint16_t* vbuf = smem + wv * (C::WAVE_BYTES / 2);
+
+  auto compute = [&](int j0, const Tile& t) {
+    // V tile -> wave-private LDS (row-major, swizzled 16-byte slots)
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int ci = lane + 64 * j;
+      const int kl = ci / DC;
+      const int slot = (ci % DC) ^ (kl % DC);
+      *reinterpret_cast<uint4*>(vbuf + kl * D + 8 * slot) = t.v[j];
+    }
+    // S^T = K Q^T for two 16-key blocks
+    f32x4 s[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[qb][kb] = f32x4{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, t.k[kb][c]), qf[qb][c], s[qb][kb], 0, 0, 0);
+      }
+    // register r of block kb holds key j0 + 16 kb + 4 grp + r
+    if (j0 + BK > wlo) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j0 + 16 * kb + 4 * grp + r >= lim[qb]) s[qb][kb][r] = -INFINITY;
+    }
+    bf16x8 pb[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float mx = fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
+                       fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m[qb], mx * a.scale_log2);
+      const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = ex2(m[qb] - mu);
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pj = ex2(__builtin_fmaf(s[qb][kb][r], a.scale_log2, -mu));
+          ls += pj;
+          pb[qb][4 * kb + r] = (__bf16)pj;
+        }
+      l[qb] = l[qb] * alpha + ls;
+      m[qb] = m_new;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
+    }
+    // O^T += V^T P^T; A operand by two transposing LDS reads per d block
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      i16x4 va[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kl = 16 * half + 4 * grp + (c16 >> 2);
+        const int slot = (2 * db + ((c16 & 3) >> 1)) ^ (kl % DC);
+        va[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vbuf + kl * D + 8 * slot + 4 * (c16 & 1)));
+      }
+      const bf16x8 vv = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(va[0], va[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[qb], acc[qb][db], 0, 0, 0);
+    }
+  };
+
+  // ---- key loop: this wave takes tiles wv, wv + NW, ...; two register tiles
+  // in rotation.  The prefetch is unconditional (past the end it re-reads the
+  // wave's last tile, which is still in L2) so no branch sits between a load
+  // and the compute that must not wait for it.
+  {
+    const int mine = wv < ntiles ? (ntiles - wv + NW - 1) / NW : 0;
+    auto tile_key = [&](int k) { return kbeg + (wv + NW * min(k, mine - 1)) * BK; };
+    if (mine > 0) {
+      Tile t0, t1;
+      load(tile_key(0), t0);
+      for (int k = 0; k < mine; k += 2) {
+        load(tile_key(k + 1), t1);
+        compute(tile_key(k), t0);
+        if (k + 1 >= mine) break;
+        load(tile_key(k + 2), t0);
+        compute(tile_key(k + 1), t1);
+      }
+    }
+  }
+
+  // ---- combine the NW waves' states through LDS (wave 0 keeps the result)
+  if constexpr (NW > 1) {
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem) + wv * (C::WAVE_BYTES / 4);
+    if (wv > 0) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float* r = red + qb * (2 + 4 * NDB) * 64;
+        r[lane] = m[qb];
+        r[64 + lane] = l[qb];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[(2 + 4 * db + e) * 64 + lane] = acc[qb][db][e];
+      }
+    }
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) {
+      const float* base = reinterpret_cast<const float*>(smem) + w2 * (C::WAVE_BYTES / 4);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float* r = base + qb * (2 + 4 * NDB) * 64;
+        const float m2 = r[lane];
+        const float l2 = r[64 + lane];
+        const float mn = fmaxf(m[qb], m2);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        const float wa = ex2(m[qb] - mu);
+        const float wb = ex2(m2 - mu);
+        l[qb] = l[qb] * wa + l2 * wb;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[qb][db][e] = acc[qb][db][e] * wa + r[(2 + 4 * db + e) * 64 + lane] * wb;
+        m[qb] = mn;
+      }
+    }
+  }
+
+  // ---- epilogue; acc[qb][db][e] holds d = 16 db + 4 grp + e of column c16
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    float lt = l[qb];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (!rvalid[qb]) continue;
+    const int p = pq[qb], h = hq[qb];
+    if constexpr (PARTIAL) {
+      int64_t row;
+      if constexpr (PAGED)
+        row = (int64_t)h * a.total_q + q_row0 + p;
+      else
+        row = ((int64_t)b * a.Hq + h) * a.Sq + p;
+      const int64_t idx = row * a.n_split + split;
+      if (grp == 0) a.ws_ml[idx] = make_float2(m[qb] == -INFINITY ? -INFINITY : m[qb] * kLn2, lt);
+      float* op = a.ws_o + idx * D + 4 * grp;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<float4*>(op + 16 * db) =
+            make_float4(acc[qb][db][0], acc[qb][db][1], acc[qb][db][2], acc[qb][db][3]);
+    } else {
+      float sl2 = -INFINITY;
+      if (a.sink) sl2 = a.sink[h] * kLog2e;
+      if (sl2 != -INFINITY) lt += ex2(sl2 - m[qb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* op;
+      if constexpr (PAGED)
+        op = a.o + (int64_t)(q_row0 + p) * a.o_ss + (int64_t)h * a.o_sh;
+      else
+        op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp) =
+            make_uint2(pack_bf16x2(acc[qb][db][0] * inv, acc[qb][db][1] * inv),
+                       pack_bf16x2(acc[qb][db][2] * inv, acc[qb][db][3] * inv));
+    }
+  }
+}
+
+}  // namespace gqa

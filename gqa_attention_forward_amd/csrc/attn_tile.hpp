@@ -1,90 +1,10 @@
-// Device kernels of libgqa: the flash-style GQA forward kernel (one template
-// over head dim, wave layout, KV addressing and epilogue) and the split-KV
-// merge kernel.  gfx950 (CDNA4) only.
-//
-// Operation (nvfp4-megamoe-kernel commit log, dsv4/kernels/attention: the
-// multi-tile FA2 commit -- running max and sum carried across KV tiles with P
-// left un-normalised, O divided by the running sum once at the end):
-//   per query row: m <- max(m, max_j s_j); alpha = e^(m_old - m);
-//   l <- alpha l + sum_j e^(s_j - m); O <- alpha O + sum_j e^(s_j - m) v_j.
-// Here every exponent is base 2 with log2(e) folded into the score scale,
-// which is the same algebra.
-//
-// Work decomposition (AstrAI commit log, the commit that packs HB = min(G,
-// warps) query heads per block so each K/V tile streams once per block):
-// one workgroup per (batch b, kv head g, q-tile, kv split).  The workgroup's
-// query rows are the flattened (position p, head-in-group hh) pairs
-// rho = p * G + hh of one kv group, so all G query heads that share kv head g
-// consume the same K/V tile from LDS.
-//
-// MFMA mapping (v_mfma_f32_32x32x16_bf16, 64-lane waves).  Each wave owns
-// 32 query rows (the MFMA N dimension) and computes S^T = K Q^T with K as the
-// A operand, so a lane holds one query row's scores for 16 keys per 32-key
-// block -- the row max/sum reductions stay in-lane plus one exchange with
-// lane ^ 32.  P^T then feeds O^T = V^T P^T as the B operand straight from the
-// accumulator registers: the K rows are read in a permuted order (bits 2 and
-// 3 of the row index swapped) so that accumulator registers 8t..8t+7 of a
-// lane hold 8 consecutive keys, which is what the B operand of the next MFMA
-// needs.  V is stored transposed in LDS (Vt[d][key]) so the A operand of the
-// P.V product is one 16-byte LDS read.
+// Workgroup-tiled GQA forward kernel: the K/V tile is shared through LDS by
+// all waves of the workgroup (prefill shapes).  See common.hpp for the math.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "common.hpp"
 
 namespace gqa {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-struct AttnArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  // element strides; dense: (b, h, s); paged Q/O: (unused, h, t)
-  int64_t q_sb, q_sh, q_ss;
-  int64_t k_sb, k_sh, k_ss;
-  int64_t v_sb, v_sh, v_ss;
-  int64_t o_sb, o_sh, o_ss;
-  const int32_t* kv_len;   // [B] or nullptr (= Skv)
-  const float* sink;       // [Hq] scaled-domain logits or nullptr
-  float2* ws_ml;           // partial mode: {m, l} per (row, split)
-  float* ws_o;             // partial mode: O~ per (row, split, d)
-  const int32_t* cu_seqlens_q;  // paged: [B + 1]
-  const int32_t* page_table;    // paged: [B, max_pages]
-  int64_t kv_sp, kv_sr;         // paged: page and in-page row strides (head stride in k_sh)
-  int32_t max_pages;
-  int32_t B, Hq, Hkv, G, Sq, Skv;
-  int32_t causal;
-  int32_t tile;       // keys per split (0 = the whole range)
-  int32_t n_split;
-  int32_t n_qtiles;   // q-tiles per (b, g)
-  float scale_log2;   // scale * log2(e), > 0
-};
-
-__device__ __forceinline__ int swap_bits23(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v;
-  v[0] = (__bf16)lo;  // round to nearest even
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float xor32_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32, 64));
-}
-__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
-
-// exp2 with the -inf convention used throughout: exp2(-inf) = 0.
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // NR row groups of 32 query rows x NK key groups of BKW keys: NR * NK waves.
 // Each iteration stages TK = NK * BKW keys of K and V in LDS; wave (rg, kg)
@@ -226,16 +146,19 @@ attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
+  // Keys at or past kend are never read: their loads go to row kend - 1
+  // (real, finite data) and the keys are masked, so they get P = 0 exactly.
+  // Branch-free loads keep the compiler's wait counts exact.
+  const int klast = kend - 1;
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int ci = tid + i * NT;
       kr[i] = make_uint4(0, 0, 0, 0);
       if (C::KCH % NT == 0 || ci < C::KCH) {
-        const int key = j0 + ci / DC;
-        if (key < kend)
-          kr[i] = *reinterpret_cast<const uint4*>(
-              row_ptr(a.k, a.k_sb, a.k_sh, a.k_ss, key) + (ci % DC) * 8);
+        const int key = min(j0 + ci / DC, klast);
+        kr[i] = *reinterpret_cast<const uint4*>(
+            row_ptr(a.k, a.k_sb, a.k_sh, a.k_ss, key) + (ci % DC) * 8);
       }
     }
 #pragma unroll
@@ -247,10 +170,9 @@ attn_fwd_kernel(const AttnArgs a) {
         const int quad = pi / DC;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = j0 + 4 * quad + r;
-          if (key < kend)
-            vr[i][r] = *reinterpret_cast<const uint4*>(
-                row_ptr(a.v, a.v_sb, a.v_sh, a.v_ss, key) + (pi % DC) * 8);
+          const int key = min(j0 + 4 * quad + r, klast);
+          vr[i][r] = *reinterpret_cast<const uint4*>(
+              row_ptr(a.v, a.v_sb, a.v_sh, a.v_ss, key) + (pi % DC) * 8);
         }
       }
     }
@@ -446,55 +368,6 @@ attn_fwd_kernel(const AttnArgs a) {
         *reinterpret_cast<uint2*>(op + 32 * db + 8 * q4 + 4 * hl) =
             make_uint2(pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
                        pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv));
-  }
-}
-
-// Split-KV merge (kernbench2 benches commit log: the (m, l, O) state and its
-// associative merge; nvfp4-megamoe-kernel commit log: normalise once).
-// One 64-lane wave per query row; D / 64 output elements per lane.
-template <int D>
-__global__ void __launch_bounds__(256)
-merge_kernel(const float2* __restrict__ ml, const float* __restrict__ ot, uint16_t* o,
-             int64_t o_sb, int64_t o_sh, int64_t o_ss, const float* sink, int Hq, int Sq,
-             int n_split, int64_t rows) {
-  constexpr int E = D / 64;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const int i = (int)(row % Sq);
-  const int h = (int)((row / Sq) % Hq);
-  const int64_t b = row / ((int64_t)Sq * Hq);
-  const float2* mlr = ml + row * n_split;
-  const float* otr = ot + row * n_split * D;
-
-  const float sk = sink ? sink[h] : -INFINITY;
-  float M = sk;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, mlr[s].x);
-  float out[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) out[e] = 0.f;
-  if (M != -INFINITY) {
-    float Lsum = (sk == -INFINITY) ? 0.f : __expf(sk - M);
-    float accv[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) accv[e] = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float2 st = mlr[s];
-      if (st.x == -INFINITY) continue;
-      const float w = __expf(st.x - M);
-      Lsum += st.y * w;
-#pragma unroll
-      for (int e = 0; e < E; ++e) accv[e] += w * otr[s * D + lane * E + e];
-    }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) out[e] = accv[e] * inv;
-  }
-  uint16_t* op = o + b * o_sb + (int64_t)h * o_sh + (int64_t)i * o_ss + lane * E;
-  if constexpr (E == 2) {
-    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(out[0], out[1]);
-  } else {
-    *reinterpret_cast<__bf16*>(op) = (__bf16)out[0];
   }
 }
 

@@ -1,0 +1,91 @@
+// Shared device definitions of libgqa's gfx950 (CDNA4) kernels: the kernel
+// argument block, bf16/MFMA vector types and small wave helpers.
+//
+// Operation (nvfp4-megamoe-kernel commit log, dsv4/kernels/attention: the
+// multi-tile FA2 commit -- running max and sum carried across KV tiles with P
+// left un-normalised, O divided by the running sum once at the end):
+//   per query row: m <- max(m, max_j s_j); alpha = e^(m_old - m);
+//   l <- alpha l + sum_j e^(s_j - m); O <- alpha O + sum_j e^(s_j - m) v_j.
+// Here every exponent is base 2 with log2(e) folded into the score scale,
+// which is the same algebra.
+//
+// Work decomposition (AstrAI commit log, the commit that packs HB = min(G,
+// warps) query heads per block so each K/V tile streams once per block):
+// one workgroup per (batch b, kv head g, q-tile, kv split).  The workgroup's
+// query rows are the flattened (position p, head-in-group hh) pairs
+// rho = p * G + hh of one kv group, so all G query heads that share kv head g
+// consume the same K/V tile from LDS.
+//
+// MFMA mapping (v_mfma_f32_32x32x16_bf16, 64-lane waves).  Each wave owns
+// 32 query rows (the MFMA N dimension) and computes S^T = K Q^T with K as the
+// A operand, so a lane holds one query row's scores for 16 keys per 32-key
+// block -- the row max/sum reductions stay in-lane plus one exchange with
+// lane ^ 32.  P^T then feeds O^T = V^T P^T as the B operand straight from the
+// accumulator registers: the K rows are read in a permuted order (bits 2 and
+// 3 of the row index swapped) so that accumulator registers 8t..8t+7 of a
+// lane hold 8 consecutive keys, which is what the B operand of the next MFMA
+// needs.  V is stored transposed in LDS (Vt[d][key]) so the A operand of the
+// P.V product is one 16-byte LDS read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  // element strides; dense: (b, h, s); paged Q/O: (unused, h, t)
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  const int32_t* kv_len;   // [B] or nullptr (= Skv)
+  const float* sink;       // [Hq] scaled-domain logits or nullptr
+  float2* ws_ml;           // partial mode: {m, l} per (row, split)
+  float* ws_o;             // partial mode: O~ per (row, split, d)
+  const int32_t* cu_seqlens_q;  // paged: [B + 1]
+  const int32_t* page_table;    // paged: [B, max_pages]
+  int64_t kv_sp, kv_sr;         // paged: page and in-page row strides (head stride in k_sh)
+  int32_t max_pages;
+  int32_t B, Hq, Hkv, G, Sq, Skv;
+  int32_t causal;
+  int32_t tile;       // keys per split (0 = the whole range)
+  int32_t n_split;
+  int32_t n_qtiles;   // q-tiles per (b, g)
+  int32_t total_q;    // paged: packed query rows (partial-state row = h * total_q + t)
+  float scale_log2;   // scale * log2(e), > 0
+};
+
+__device__ __forceinline__ int swap_bits23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;  // round to nearest even
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float xor32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// exp2 with the -inf convention used throughout: exp2(-inf) = 0.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace gqa

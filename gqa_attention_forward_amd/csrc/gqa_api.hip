@@ -13,7 +13,9 @@
 #include <cstdio>
 #include <mutex>
 
-#include "attn_kernels.hpp"
+#include "attn_stream.hpp"
+#include "attn_tile.hpp"
+#include "merge.hpp"
 #include "gqa.h"
 
 namespace {
@@ -88,36 +90,60 @@ gqa_status_t check_launch(const char* what) {
   return GQA_OK;
 }
 
-template <int D, int NR, int NK, int BKW, bool PAGED, bool PARTIAL>
-gqa_status_t launch_attn(gqa::AttnArgs args, int64_t q_rows_per_bg, hipStream_t stream) {
-  using C = gqa::Cfg<D, NR, NK, BKW>;
-  auto* kern = &gqa::attn_fwd_kernel<D, NR, NK, BKW, PAGED, PARTIAL>;
-  // dynamic LDS above 64 KiB has to be allowed once per kernel instantiation
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-  });
-  if (attr_err != hipSuccess)
-    return fail(GQA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
-  args.n_qtiles = (int32_t)cdiv(q_rows_per_bg, NR * 32);
+// Launch one attention kernel instantiation over the (b, g, split, q-tile)
+// grid; `rows_per_tile` query rows of a kv group per workgroup.
+template <class K>
+gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args,
+                         int64_t q_rows_per_bg, int rows_per_tile, hipStream_t stream) {
+  // dynamic LDS above 64 KiB has to be allowed once per kernel; the cache
+  // is keyed by the kernel address
+  static std::mutex mu;
+  static const void* done[64];
+  static int ndone = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    bool seen = false;
+    for (int i = 0; i < ndone; ++i) seen |= done[i] == reinterpret_cast<const void*>(kern);
+    if (!seen) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+      if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+      if (ndone < 64) done[ndone++] = reinterpret_cast<const void*>(kern);
+    }
+  }
+  args.n_qtiles = (int32_t)cdiv(q_rows_per_bg, rows_per_tile);
   const int64_t nblocks = (int64_t)args.B * args.Hkv * args.n_split * args.n_qtiles;
   if (nblocks <= 0) return GQA_OK;
   if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large (%lld)", (long long)nblocks);
   (void)hipGetLastError();  // clear a stale error so the check below is ours
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(C::NT), C::LDS_BYTES, stream, args);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(threads), lds_bytes, stream, args);
   return check_launch("attention kernel");
 }
 
-// Wave layout by query rows per (b, kv head): decode-like groups (<= 32 rows)
-// put the waves on different keys of a shared tile, large groups put them on
-// different rows.
+template <int D, int NR, int NK, int BKW, bool PAGED, bool PARTIAL>
+gqa_status_t launch_tile(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+  using C = gqa::Cfg<D, NR, NK, BKW>;
+  return launch_grid(&gqa::attn_fwd_kernel<D, NR, NK, BKW, PAGED, PARTIAL>, C::LDS_BYTES, C::NT,
+                     args, rows, NR * 32, stream);
+}
+
+template <int D, int NQB, bool PAGED, bool PARTIAL>
+gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+  using C = gqa::StreamCfg<D, NQB>;
+  constexpr int NW = 4;
+  return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL>, NW * C::WAVE_BYTES,
+                     NW * 64, args, rows, 16 * NQB, stream);
+}
+
+// Kernel choice by query rows per (b, kv head): groups of up to 32 rows
+// (decode, short query blocks) stream keys per wave; larger groups share
+// K/V tiles across the waves of a workgroup.
 template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  if (rows <= 32) return launch_attn<D, 1, 2, 32, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 64) return launch_attn<D, 2, 2, 32, PAGED, PARTIAL>(args, rows, stream);
-  return launch_attn<D, 4, 1, 64, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 32) return launch_stream<D, 2, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 64) return launch_tile<D, 2, 2, 32, PAGED, PARTIAL>(args, rows, stream);
+  return launch_tile<D, 4, 1, 64, PAGED, PARTIAL>(args, rows, stream);
 }
 
 template <bool PAGED, bool PARTIAL>

@@ -39,8 +39,7 @@ struct StreamCfg {
   static constexpr int VPL = BK * DC / 64;  // V chunks per lane per tile
   static constexpr int VTILE = BK * D;      // V tile elements (per wave)
   static constexpr int SLOT_F = NQB * (2 + 4 * NDB) * 64;  // combine floats per wave
-  static constexpr int WAVE_BYTES =
-      (VTILE * 2 > SLOT_F * 4 ? VTILE * 2 : SLOT_F * 4);
+  static constexpr int WAVE_BYTES = (VTILE * 2 > SLOT_F * 4 ? VTILE * 2 : SLOT_F * 4);
 };
 
 // Two waves per SIMD for one 16-column block; one for two blocks (the second
@@ -188,9 +187,9 @@ attn_stream_kernel(const AttnArgs a) {
     // S^T = K Q^T for two 16-key blocks
     f32x4 s[NQB][2];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int qb = 0; qb < NQB; ++qb) {
         s[qb][kb] = f32x4{};
 #pragma unroll
         for (int c = 0; c < NC; ++c)

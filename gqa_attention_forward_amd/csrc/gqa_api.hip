@@ -127,12 +127,40 @@ gqa_status_t launch_tile(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
                      args, rows, NR * 32, stream);
 }
 
-template <int D, int NQB, bool PAGED, bool PARTIAL>
-gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <int D, int NQB, int NW, bool PAGED, bool PARTIAL>
+gqa_status_t launch_stream_nw(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   using C = gqa::StreamCfg<D, NQB>;
-  constexpr int NW = 4;
   return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL>, NW * C::WAVE_BYTES,
                      NW * 64, args, rows, 16 * NQB, stream);
+}
+
+// Waves per workgroup: the most waves that still let every workgroup be
+// resident at once (8 waves per CU at two waves per SIMD), so no workgroup
+// waits for a second round; 4 when even that does not fit.
+template <int D, int NQB, bool PAGED, bool PARTIAL>
+gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+  const int64_t nblocks = (int64_t)args.B * args.Hkv * args.n_split * cdiv(rows, 16 * NQB);
+  const int64_t waves_per_cu = NQB == 1 ? 8 : 4;
+  const int64_t slots = (int64_t)device_cus() * waves_per_cu;
+  if (nblocks * 4 <= slots || nblocks * 2 > slots)
+    return launch_stream_nw<D, NQB, 4, PAGED, PARTIAL>(args, rows, stream);
+  return launch_stream_nw<D, NQB, 2, PAGED, PARTIAL>(args, rows, stream);
 }
 
 // Kernel choice by query rows per (b, kv head): groups of up to 32 rows

@@ -1,0 +1,323 @@
+// Prefill GQA forward kernel: query groups of more than 32 rows per
+// (b, kv head).  One workgroup per (b, kv head g, q-tile of 32 * NW rows,
+// kv split); all NW waves share each 64-key K/V tile through LDS, so a tile
+// is fetched once per workgroup for every query head of the group (AstrAI
+// commit log, the commit that packs HB = min(G, warps) query heads per
+// block).
+//
+// MFMA mapping, v_mfma_f32_32x32x16_bf16, 32 query rows per wave (the MFMA
+// N dimension):
+//   S^T = K Q^T  : A = K rows from LDS, read in a permuted row order (bits 2
+//                  and 3 of the row index swapped) so that accumulator
+//                  registers 8t..8t+7 of a lane hold 8 consecutive keys;
+//                  B = Q in registers.  A lane holds one query row's scores,
+//                  so row max/sum reductions are in-lane plus one exchange
+//                  with lane ^ 32.
+//   O^T += V^T P^T: B = P straight from the S^T accumulators (bf16), A = V^T
+//                  gathered from the row-major V tile with two
+//                  ds_read_b64_tr_b16 per MFMA (within each 16-lane group,
+//                  destination lane i, element e comes from source lane
+//                  4e + i/4, element i%4).
+// K and V tiles are stored row-major without padding; their 16-byte slots
+// are XOR-swizzled per row (K: row % (D/8); V: 2(row % 4) ^ 8 bit3(row)) so
+// the row writes, the K operand reads and the transposing V reads are all
+// bank-conflict free.
+//
+// Online softmax in base 2 with a lazily moved reference: a row's reference
+// m only moves when the tile max exceeds it by more than 8 (log2 units), so
+// the O / l rescale is skipped on most tiles; P = 2^(s - m) <= 2^8 then.
+// The algebra is unchanged -- (m, l, O) stay consistent -- and the final
+// division by l happens once (nvfp4-megamoe-kernel commit log, multi-tile
+// FA2 and normalise-once commits).
+#pragma once
+
+#include "common.hpp"
+
+namespace gqa {
+
+template <int D, int NW>
+struct PrefillCfg {
+  static constexpr int BK = 64;              // keys per tile
+  static constexpr int DC = D / 8;           // 16-byte chunks per row
+  static constexpr int NT = NW * 64;
+  static constexpr int TILE = BK * D;        // elements of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;     // K then V
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int CPT = BK * DC / NT;   // chunks per thread per tensor
+  static_assert(CPT >= 1 && BK * DC % NT == 0, "tile split");
+};
+
+__device__ __forceinline__ int vswz(int key, int dc) {
+  return ((2 * (key & 3)) ^ (((key >> 3) & 1) << 3)) & (dc - 1);
+}
+
+constexpr float kLazyRescale = 8.f;  // log2 units
+
+template <int D, int NW, bool PAGED, bool PARTIAL>
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_prefill_kernel(const AttnArgs a) {
+  using C = PrefillCfg<D, NW>;
+  constexpr int NT = C::NT;
+  constexpr int BK = C::BK;
+  constexpr int DC = C::DC;
+  constexpr int CPT = C::CPT;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int col = lane & 31;
+  const int hl = lane >> 5;
+
+  const int L = blockIdx.x;
+  const int nbg = a.B * a.Hkv;
+  const int bg = L % nbg;
+  const int rest = L / nbg;
+  const int split = rest % a.n_split;
+  const int qt = a.n_qtiles - 1 - rest / a.n_split;  // late (heavy causal) q-tiles first
+  const int b = bg / a.Hkv;
+  const int g = bg % a.Hkv;
+  const int G = a.G;
+
+  int q_len, q_row0 = 0;
+  if constexpr (PAGED) {
+    q_row0 = a.cu_seqlens_q[b];
+    q_len = a.cu_seqlens_q[b + 1] - q_row0;
+  } else {
+    q_len = a.Sq;
+  }
+  int n = a.Skv;
+  if (a.kv_len) n = min(max(a.kv_len[b], 0), a.Skv);
+  const int rows_total = q_len * G;
+  const int row0 = qt * (32 * NW);
+  if (row0 >= rows_total) return;
+
+  int kbeg = 0, kend = n;
+  if (a.tile > 0) {
+    kbeg = split * a.tile;
+    kend = min(n, kbeg + a.tile);
+  }
+  if (a.causal) {
+    const int p_last = (min(row0 + 32 * NW, rows_total) - 1) / G;
+    kend = min(kend, min(max(n - q_len + p_last + 1, 0), n));
+  }
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  // ---- this lane's query row and the wave's masking bounds
+  const int rho = row0 + 32 * wv + col;
+  const bool rvalid = rho < rows_total;
+  const int p = rvalid ? rho / G : 0;
+  const int h = g * G + (rvalid ? rho - p * G : 0);
+  int lim = kend;
+  if (a.causal) lim = min(kend, min(max(n - q_len + p + 1, 0), n));
+  const int wrow0 = row0 + 32 * wv;
+  int wlo = kend;  // below wlo no row of the wave is masked
+  if (a.causal) wlo = min(kend, min(max(n - q_len + wrow0 / G + 1, 0), n));
+  if (wrow0 >= rows_total) wlo = kbeg;
+
+  // ---- Q operand: lane holds query row `col`, d = 16 c + 8 hl + e
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp;
+    if constexpr (PAGED)
+      qp = a.q + (int64_t)(q_row0 + p) * a.q_ss + (int64_t)h * a.q_sh;
+    else
+      qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)p * a.q_ss;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qf[c] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hl) : bf16x8{};
+  }
+
+  float sl2 = -INFINITY;  // sink in log2 units (final mode)
+  if constexpr (!PARTIAL)
+    if (a.sink && rvalid) sl2 = a.sink[h] * kLog2e;
+  float mref = sl2;        // reference the running sums are taken against
+  float mtrue = sl2;       // true running max (for the partial epilogue)
+  float l = 0.f;           // this lane's share of the running sum
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+  // ---- K/V staging: chunk ci = tid + i NT of a 64 x DC tile.  Keys at or
+  // past kend are never read (loads go to row kend - 1, the keys are masked)
+  auto krow = [&](int key) -> const uint16_t* {
+    if constexpr (PAGED) {
+      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
+      return a.k + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.k_sh;
+    } else {
+      return a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)key * a.k_ss;
+    }
+  };
+  auto vrow = [&](int key) -> const uint16_t* {
+    if constexpr (PAGED) {
+      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
+      return a.v + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.v_sh;
+    } else {
+      return a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)key * a.v_ss;
+    }
+  };
+  const int klast = kend - 1;
+  struct Stage {
+    u32x4 k[CPT];
+    u32x4 v[CPT];
+  };
+  auto load_tile = [&](int j0, Stage& st) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * NT;
+      const int key = min(j0 + ci / DC, klast);
+      st.k[i] = *reinterpret_cast<const u32x4*>(krow(key) + 8 * (ci % DC));
+      st.v[i] = *reinterpret_cast<const u32x4*>(vrow(key) + 8 * (ci % DC));
+    }
+  };
+  auto store_tile = [&](int stage, const Stage& st) {
+    uint16_t* Ks = smem + stage * C::STAGE;
+    uint16_t* Vs = Ks + C::TILE;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / DC, ch = ci % DC;
+      *reinterpret_cast<u32x4*>(Ks + row * D + 8 * (ch ^ (row % DC))) = st.k[i];
+      *reinterpret_cast<u32x4*>(Vs + row * D + 8 * (ch ^ vswz(row, DC))) = st.v[i];
+    }
+  };
+
+  Stage nx;
+  if (ntiles > 0) {
+    load_tile(kbeg, nx);
+    store_tile(0, nx);
+  }
+  __syncthreads();
+
+  const int krow_a = swap_bits23(col);  // K row (within a 32-key block) this lane feeds to MFMA
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = kbeg + it * BK;
+    // unconditional prefetch (past the end it re-reads the last tile, an L2
+    // hit): with no branch around it the compiler keeps it in registers
+    load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
+
+    {
+      const uint16_t* Ks = smem + (it & 1) * C::STAGE;
+      const uint16_t* Vs = Ks + C::TILE;
+
+      // two independent accumulation chains, interleaved
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int row = 32 * mb + krow_a;
+          const bf16x8 kk =
+              *reinterpret_cast<const bf16x8*>(Ks + row * D + 8 * ((2 * c + hl) ^ (row % DC)));
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qf[c], s[mb], 0, 0, 0);
+        }
+      // register j of block mb holds key j0 + 32 mb + 16 (j >> 3) + 8 hl + (j & 7)
+      if (j0 + BK > wlo) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (j0 + 32 * mb + 16 * (j >> 3) + 8 * hl + (j & 7) >= lim) s[mb][j] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
+      mx = xor32_max(mx) * a.scale_log2;
+      mtrue = fmaxf(mtrue, mx);
+      const bool move = mx > mref + kLazyRescale;
+      if (__any(move)) {
+        const float alpha = move ? ex2(mref - mx) : 1.f;  // 0 when mref = -inf
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[db][j] *= alpha;
+        mref = move ? mx : mref;
+      }
+      const float mu = (mref == -INFINITY) ? 0.f : mref;
+      bf16x8 pb[4];
+      float ls = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 pj = (__bf16)ex2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + e], a.scale_log2, -mu));
+          pb[t][e] = pj;
+          ls += (float)pj;  // the sum uses the same rounded weights as P.V
+        }
+      l += ls;
+
+      // O^T += V^T P^T
+      const int g16 = lane >> 4;
+      const int r16 = lane & 15;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int cc = 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
+          i16x4 va[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int key = 16 * t + 8 * hl + 4 * half + (r16 >> 2);
+            va[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(Vs + key * D +
+                                                           8 * ((cc >> 3) ^ vswz(key, DC)) +
+                                                           (cc & 7)));
+          }
+          const bf16x8 vv = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(va[0], va[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[t], acc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    store_tile((it + 1) & 1, nx);
+    __syncthreads();
+  }
+
+  // ---- epilogue; accumulator register j of d-block db holds
+  //      d = 32 db + 8 (j >> 2) + 4 hl + (j & 3) of query row `col`
+  float lt = xor32_sum(l);
+  if constexpr (PARTIAL) {
+    // report the state against the true max (as the partial format states)
+    const float f = (mtrue == -INFINITY) ? 0.f : ex2(mref - mtrue);
+    lt *= f;
+    if (!rvalid) return;
+    int64_t row;
+    if constexpr (PAGED)
+      row = (int64_t)h * a.total_q + q_row0 + p;
+    else
+      row = ((int64_t)b * a.Hq + h) * a.Sq + p;
+    const int64_t idx = row * a.n_split + split;
+    if (hl == 0) a.ws_ml[idx] = make_float2(mtrue == -INFINITY ? -INFINITY : mtrue * kLn2, lt);
+    float* op = a.ws_o + idx * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * q4 + 4 * hl) =
+            make_float4(acc[db][4 * q4] * f, acc[db][4 * q4 + 1] * f, acc[db][4 * q4 + 2] * f,
+                        acc[db][4 * q4 + 3] * f);
+  } else {
+    if (sl2 != -INFINITY) lt += ex2(sl2 - mref);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (!rvalid) return;
+    uint16_t* op;
+    if constexpr (PAGED)
+      op = a.o + (int64_t)(q_row0 + p) * a.o_ss + (int64_t)h * a.o_sh;
+    else
+      op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * q4 + 4 * hl) =
+            make_uint2(pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                       pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv));
+  }
+}
+
+}  // namespace gqa

@@ -221,9 +221,9 @@ attn_stream_kernel(const AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pj = ex2(__builtin_fmaf(s[qb][kb][r], a.scale_log2, -mu));
-          ls += pj;
-          pb[qb][4 * kb + r] = (__bf16)pj;
+          const __bf16 pj = (__bf16)ex2(__builtin_fmaf(s[qb][kb][r], a.scale_log2, -mu));
+          pb[qb][4 * kb + r] = pj;
+          ls += (float)pj;  // the sum uses the same rounded weights as P.V
         }
       l[qb] = l[qb] * alpha + ls;
       m[qb] = m_new;

@@ -14,7 +14,7 @@
 #include <mutex>
 
 #include "attn_stream.hpp"
-#include "attn_tile.hpp"
+#include "attn_prefill.hpp"
 #include "merge.hpp"
 #include "gqa.h"
 
@@ -120,11 +120,11 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
   return check_launch("attention kernel");
 }
 
-template <int D, int NR, int NK, int BKW, bool PAGED, bool PARTIAL>
-gqa_status_t launch_tile(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  using C = gqa::Cfg<D, NR, NK, BKW>;
-  return launch_grid(&gqa::attn_fwd_kernel<D, NR, NK, BKW, PAGED, PARTIAL>, C::LDS_BYTES, C::NT,
-                     args, rows, NR * 32, stream);
+template <int D, int NW, bool PAGED, bool PARTIAL>
+gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+  using C = gqa::PrefillCfg<D, NW>;
+  return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL>, C::LDS_BYTES, C::NT, args,
+                     rows, 32 * NW, stream);
 }
 
 // Compute units of the current device (queried once per device).
@@ -165,13 +165,14 @@ gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
 
 // Kernel choice by query rows per (b, kv head): groups of up to 32 rows
 // (decode, short query blocks) stream keys per wave; larger groups share
-// K/V tiles across the waves of a workgroup.
+// K/V tiles across the waves of a workgroup, 32 rows per wave.
 template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
   if (rows <= 32) return launch_stream<D, 2, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 64) return launch_tile<D, 2, 2, 32, PAGED, PARTIAL>(args, rows, stream);
-  return launch_tile<D, 4, 1, 64, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 64) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 128) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
+  return launch_prefill<D, 8, PAGED, PARTIAL>(args, rows, stream);
 }
 
 template <bool PAGED, bool PARTIAL>

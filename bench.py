@@ -207,6 +207,35 @@ def bench_secondary(args, device, stream):
     return res
 
 
+def run_only(args, device, stream):
+    """One workload's kernels alone (for counter collection under rocprofv3)."""
+    name = args.only
+    if name == "copy":
+        # calibration for HBM byte counters: a plain 256 MiB device copy
+        x = torch.empty(128 << 20, dtype=torch.bfloat16, device=device).fill_(1.0)
+        y = torch.empty_like(x)
+        ms = time_loop(lambda: y.copy_(x), args.steps, args.warmup, stream)
+        return {"workload": name, "ms": ms, "bytes_read": x.numel() * 2, "bytes_written": y.numel() * 2}
+    if name == "decode_partial":
+        c, _, g = setup_dense("decode_splitkv", device)
+        _, partial, _, _ = decode_step_fns(g, c)
+        ms = time_loop(partial, args.steps, args.warmup, stream)
+        return {"workload": name, "ms": ms, "GB/s": dense_bytes(c)[1] / (ms * 1e-3) / 1e9}
+    if name == "ragged_paged":
+        w = workloads.make_paged()
+        gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
+        m = gqa()
+        fn = lambda: m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],  # noqa: E731
+                             gw["page_table"], gw["kv_len"], max_q_len=w["max_q_len"],
+                             scale=w["scale"], sink=gw["sink"])
+        return {"workload": name, "ms": time_loop(fn, args.steps, args.warmup, stream)}
+    c, _, g = setup_dense(name, device)
+    step, _ = prefill_step_fn(g, c, 2048 if name == "shortq_longkv" else 0)
+    ms = time_loop(step, args.steps, args.warmup, stream)
+    return {"workload": name, "ms": ms, "TFLOP/s": dense_flops(c) / (ms * 1e-3) / 1e12,
+            "GB/s": dense_bytes(c)[0] / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(inp, c, budget_s):
     """The oracle on this host's cores, cycling over whole decode sequences
     (all heads and keys of one sequence per call) until ~budget_s seconds of
@@ -244,6 +273,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
+    ap.add_argument("--only", choices=["decode_partial", "shortq_longkv", "causal_prefill",
+                                       "ragged_paged", "copy"],
+                    help="profiling aid: time only this workload's kernels and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -255,6 +287,9 @@ def main():
     device = torch.device("cuda:0")
     stream = torch.cuda.Stream(device)
     torch.cuda.synchronize()
+    if args.only:
+        print(json.dumps(run_only(args, device, stream)), flush=True)
+        return
 
     c, inp, dec = bench_decode(args, device, stream)
     secondary = None if args.no_secondary else bench_secondary(args, device, stream)

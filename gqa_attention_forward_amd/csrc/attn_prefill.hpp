@@ -18,10 +18,11 @@
 //                  ds_read_b64_tr_b16 per MFMA (within each 16-lane group,
 //                  destination lane i, element e comes from source lane
 //                  4e + i/4, element i%4).
-// K and V tiles are stored row-major without padding; their 16-byte slots
-// are XOR-swizzled per row (K: row % (D/8); V: 2(row % 4) ^ 8 bit3(row)) so
+// K tiles are stored row-major with a padded pitch (D + 8 elements), V tiles
+// row-major unpadded with 16-byte slots XOR-swizzled per row (vslot_swz), so
 // the row writes, the K operand reads and the transposing V reads are all
-// bank-conflict free.
+// bank-conflict free (checked with the LDS bank-conflict counter), and K
+// operand addresses are one base plus immediate offsets.
 //
 // Online softmax in base 2 with a lazily moved reference: a row's reference
 // m only moves when the tile max exceeds it by more than 8 (log2 units), so
@@ -37,19 +38,19 @@ namespace gqa {
 
 template <int D, int NW>
 struct PrefillCfg {
+  static constexpr bool PP = false;          // ping-pong schedule: measured slower, kept off
+  static constexpr int NSTAGE = PP ? 3 : 2;  // K/V tiles resident in LDS
   static constexpr int BK = 64;              // keys per tile
   static constexpr int DC = D / 8;           // 16-byte chunks per row
   static constexpr int NT = NW * 64;
-  static constexpr int TILE = BK * D;        // elements of one K (or V) tile
-  static constexpr int STAGE = 2 * TILE;     // K then V
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int KP = D + 8;           // K row pitch (elements): padded, not swizzled
+  static constexpr int KTILE = BK * KP;      // elements of one K tile
+  static constexpr int TILE = BK * D;        // elements of one V tile
+  static constexpr int STAGE = KTILE + TILE; // K then V
+  static constexpr int LDS_BYTES = NSTAGE * STAGE * 2;
   static constexpr int CPT = BK * DC / NT;   // chunks per thread per tensor
   static_assert(CPT >= 1 && BK * DC % NT == 0, "tile split");
 };
-
-__device__ __forceinline__ int vswz(int key, int dc) {
-  return ((2 * (key & 3)) ^ (((key >> 3) & 1) << 3)) & (dc - 1);
-}
 
 constexpr float kLazyRescale = 8.f;  // log2 units
 
@@ -172,13 +173,13 @@ attn_prefill_kernel(const AttnArgs a) {
   };
   auto store_tile = [&](int stage, const Stage& st) {
     uint16_t* Ks = smem + stage * C::STAGE;
-    uint16_t* Vs = Ks + C::TILE;
+    uint16_t* Vs = Ks + C::KTILE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int ci = tid + i * NT;
       const int row = ci / DC, ch = ci % DC;
-      *reinterpret_cast<u32x4*>(Ks + row * D + 8 * (ch ^ (row % DC))) = st.k[i];
-      *reinterpret_cast<u32x4*>(Vs + row * D + 8 * (ch ^ vswz(row, DC))) = st.v[i];
+      *reinterpret_cast<u32x4*>(Ks + row * C::KP + 8 * ch) = st.k[i];
+      *reinterpret_cast<u32x4*>(Vs + row * D + 8 * (ch ^ vslot_swz<DC>(row))) = st.v[i];
     }
   };
 
@@ -187,95 +188,143 @@ attn_prefill_kernel(const AttnArgs a) {
     load_tile(kbeg, nx);
     store_tile(0, nx);
   }
-  __syncthreads();
+  lds_barrier();
 
   const int krow_a = swap_bits23(col);  // K row (within a 32-key block) this lane feeds to MFMA
+  const int g16 = lane >> 4;
+  const int r16 = lane & 15;
+  f32x16 s[2];   // S^T of one tile: register j of block mb = key 32 mb + 16 (j >> 3) + 8 hl + (j & 7)
+  bf16x8 pb[4];  // P of one tile as the B operand of four 16-key MFMA steps
+  auto stage_of = [&](int i) -> const uint16_t* { return smem + (i % C::NSTAGE) * C::STAGE; };
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int j0 = kbeg + it * BK;
-    // unconditional prefetch (past the end it re-reads the last tile, an L2
-    // hit): with no branch around it the compiler keeps it in registers
-    load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
-
-    {
-      const uint16_t* Ks = smem + (it & 1) * C::STAGE;
-      const uint16_t* Vs = Ks + C::TILE;
-
-      // two independent accumulation chains, interleaved
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+  // S^T = K Q^T for tile i (two interleaved accumulation chains), masked
+  auto qk = [&](int i) {
+    const uint16_t* Ks = stage_of(i);
+    const int j0 = kbeg + i * BK;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c)
+    for (int c = 0; c < D / 16; ++c)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int row = 32 * mb + krow_a;
-          const bf16x8 kk =
-              *reinterpret_cast<const bf16x8*>(Ks + row * D + 8 * ((2 * c + hl) ^ (row % DC)));
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qf[c], s[mb], 0, 0, 0);
-        }
-      // register j of block mb holds key j0 + 32 mb + 16 (j >> 3) + 8 hl + (j & 7)
-      if (j0 + BK > wlo) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (j0 + 32 * mb + 16 * (j >> 3) + 8 * hl + (j & 7) >= lim) s[mb][j] = -INFINITY;
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kk = *reinterpret_cast<const bf16x8*>(Ks + (32 * mb + krow_a) * C::KP +
+                                                           16 * c + 8 * hl);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qf[c], s[mb], 0, 0, 0);
       }
-      float mx = -INFINITY;
+    if (__builtin_expect(j0 + BK > wlo, 0)) {
+      const int rem = lim - j0 - 8 * hl;  // first masked offset of this lane
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
-      mx = xor32_max(mx) * a.scale_log2;
-      mtrue = fmaxf(mtrue, mx);
-      const bool move = mx > mref + kLazyRescale;
-      if (__any(move)) {
-        const float alpha = move ? ex2(mref - mx) : 1.f;  // 0 when mref = -inf
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) acc[db][j] *= alpha;
-        mref = move ? mx : mref;
-      }
-      const float mu = (mref == -INFINITY) ? 0.f : mref;
-      bf16x8 pb[4];
-      float ls = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 pj = (__bf16)ex2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + e], a.scale_log2, -mu));
-          pb[t][e] = pj;
-          ls += (float)pj;  // the sum uses the same rounded weights as P.V
-        }
-      l += ls;
+        for (int j = 0; j < 16; ++j)
+          if (32 * mb + 16 * (j >> 3) + (j & 7) >= rem) s[mb][j] = -INFINITY;
+    }
+  };
 
-      // O^T += V^T P^T
-      const int g16 = lane >> 4;
-      const int r16 = lane & 15;
+  // online softmax of the tile in s: P -> pb, running (m, l) and the O rescale
+  auto softmax = [&]() {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int cc = 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
-          i16x4 va[2];
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
+    mx = xor32_max(mx) * a.scale_log2;
+    mtrue = fmaxf(mtrue, mx);
+    const bool move = mx > mref + kLazyRescale;
+    if (__any(move)) {
+      const float alpha = move ? ex2(mref - mx) : 1.f;  // 0 when mref = -inf
+      l *= alpha;
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int key = 16 * t + 8 * hl + 4 * half + (r16 >> 2);
-            va[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(Vs + key * D +
-                                                           8 * ((cc >> 3) ^ vswz(key, DC)) +
-                                                           (cc & 7)));
-          }
-          const bf16x8 vv = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(va[0], va[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[t], acc[db], 0, 0, 0);
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[db][j] *= alpha;
+      mref = move ? mx : mref;
+    }
+    const float mu = (mref == -INFINITY) ? 0.f : mref;
+    // P rounded to bf16 in pairs; the row sum is taken over the same rounded
+    // values with a packed dot against (1, 1)
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        bf16x2 pp;
+        pp[0] = (__bf16)ex2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + e], a.scale_log2, -mu));
+        pp[1] = (__bf16)ex2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + e + 1], a.scale_log2, -mu));
+        pb[t][e] = pp[0];
+        pb[t][e + 1] = pp[1];
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
+      }
+    l += ls;
+  };
+
+  // O^T += V^T P^T for tile i
+  auto pv = [&](int i) {
+    const uint16_t* Vs = stage_of(i) + C::KTILE;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int cc = 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
+        i16x4 va[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int key = 16 * t + 8 * hl + 4 * half + (r16 >> 2);
+          va[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(Vs + key * D +
+                                                         8 * ((cc >> 3) ^ vslot_swz<DC>(key)) +
+                                                         (cc & 7)));
         }
+        const bf16x8 vv = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(va[0], va[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[t], acc[db], 0, 0, 0);
       }
     }
+  };
 
-    store_tile((it + 1) & 1, nx);
-    __syncthreads();
+  // The prefetch of the next tile is unconditional (past the end it re-reads
+  // the last tile, an L2 hit): with no branch around it, the compiler keeps
+  // it ahead of the compute instead of sinking it to its LDS store.
+  if constexpr (!C::PP) {
+    for (int it = 0; it < ntiles; ++it) {
+      load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
+      qk(it);
+      softmax();
+      pv(it);
+      store_tile((it + 1) % C::NSTAGE, nx);
+      lds_barrier();
+    }
+  } else {
+    // Ping-pong: waves 0-3 and 4-7 share the four SIMDs pairwise.  Each
+    // iteration has two phases; in each, one group issues its MFMA work
+    // (P.V of the previous tile, then Q.K of this one) while the other runs
+    // the softmax VALU work, so the matrix and vector pipes of a SIMD are fed
+    // by different waves.  Tiles it - 1 (its V) and it (its K) are resident;
+    // tile it + 1 is staged into the third LDS slot.
+    const bool grp_a = wv < 4;
+    constexpr bool PRIO = true;
+    for (int it = 0; it <= ntiles; ++it) {
+      load_tile(kbeg + min(it + 1, max(ntiles - 1, 0)) * BK, nx);
+      if (grp_a) {
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
+        if (it >= 1) pv(it - 1);
+        if (it < ntiles) qk(it);
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
+      } else if (it >= 1) {
+        softmax();  // of tile it - 1, whose S^T this group computed last phase
+      }
+      lds_barrier();
+      if (grp_a) {
+        if (it < ntiles) softmax();
+      } else {
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
+        if (it >= 1) pv(it - 1);
+        if (it < ntiles) qk(it);
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
+      }
+      if (it + 1 < ntiles) store_tile((it + 1) % C::NSTAGE, nx);
+      lds_barrier();
+    }
   }
 
   // ---- epilogue; accumulator register j of d-block db holds

@@ -22,7 +22,7 @@
 //                         lane 4e + i/4, element i%4 -- so each source lane
 //                         points at 4 d of one key row and every lane gets 4
 //                         keys of one d).
-//   16-byte V slots in LDS are XOR-swizzled by (key % (D/8)), which makes
+//   16-byte V slots in LDS are XOR-swizzled per row (vslot_swz), which makes
 //   both the b128 row writes and the transposing reads bank-conflict free.
 #pragma once
 
@@ -181,7 +181,7 @@ attn_stream_kernel(const AttnArgs a) {
     for (int j = 0; j < VPL; ++j) {
       const int ci = lane + 64 * j;
       const int kl = ci / DC;
-      const int slot = (ci % DC) ^ (kl % DC);
+      const int slot = (ci % DC) ^ vslot_swz<DC>(kl);
       *reinterpret_cast<uint4*>(vbuf + kl * D + 8 * slot) = t.v[j];
     }
     // S^T = K Q^T for two 16-key blocks
@@ -237,7 +237,7 @@ attn_stream_kernel(const AttnArgs a) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int kl = 16 * half + 4 * grp + (c16 >> 2);
-        const int slot = (2 * db + ((c16 & 3) >> 1)) ^ (kl % DC);
+        const int slot = (2 * db + ((c16 & 3) >> 1)) ^ vslot_swz<DC>(kl);
         va[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vbuf + kl * D + 8 * slot + 4 * (c16 & 1)));
       }

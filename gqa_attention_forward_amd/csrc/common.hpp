@@ -38,6 +38,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// (1.0, 1.0) in bf16: v_dot2 against it sums a packed pair in fp32
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -74,7 +78,6 @@ __device__ __forceinline__ int swap_bits23(int r) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v;
   v[0] = (__bf16)lo;  // round to nearest even
   v[1] = (__bf16)hi;
@@ -85,6 +88,29 @@ __device__ __forceinline__ float xor32_max(float x) {
   return fmaxf(x, __shfl_xor(x, 32, 64));
 }
 __device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// XOR swizzle of the 16-byte slots of a row-major V tile row `key` (DC slots
+// per row).  Measured on gfx950: ds_read_b64_tr_b16 is served per 32-lane
+// half-wave from 64 four-byte banks, so the four (prefill) or eight (stream)
+// key rows one half-wave gathers from must land on disjoint slot groups;
+// this swizzle makes both gather shapes, and the b128 row writes,
+// bank-conflict free.
+template <int DC>
+__device__ __forceinline__ int vslot_swz(int key) {
+  if constexpr (DC == 16)
+    return ((key & 3) << 2) | (((key >> 2) & 1) << 1);
+  else
+    return (((key >> 1) & 1) << 2) | (((key >> 2) & 1) << 1);
+}
+
+// Workgroup barrier that orders LDS only: global loads in flight (prefetch)
+// stay in flight across it, unlike __syncthreads(), whose fence also waits
+// for them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // exp2 with the -inf convention used throughout: exp2(-inf) = 0.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }

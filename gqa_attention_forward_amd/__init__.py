@@ -160,8 +160,13 @@ def splitkv_merge(workspace, *, B, Hq, Sq, d, n_split, sink=None, out=None, devi
 
 
 def paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, *, max_q_len, scale=None,
-          sink=None, causal=False, page_size=64, out=None):
-    """Ragged-Q paged-KV attention: q [total_q, Hq, d]; pools [n_pages, 64, Hkv, d]."""
+          sink=None, causal=False, page_size=64, tile_s_kv=0, out=None, workspace=None):
+    """Ragged-Q paged-KV attention: q [total_q, Hq, d]; pools [n_pages, 64, Hkv, d].
+
+    tile_s_kv > 0 splits each sequence's keys into tiles of that many keys
+    (partial states + merge kernel), which spreads long sequences over more
+    workgroups.
+    """
     _need_dev("q", q, torch.bfloat16)
     _need_dev("k_cache", k_cache, torch.bfloat16)
     _need_dev("v_cache", v_cache, torch.bfloat16)
@@ -180,13 +185,17 @@ def paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, *, max_q_len, s
     total_q, Hq, d = q.shape
     B = cu_seqlens_q.numel() - 1
     Hkv = k_cache.shape[2]
+    max_pages = page_table.shape[1]
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    nbytes = workspace_size(1, Hq, total_q, max_pages * page_size, d, tile_s_kv)
+    workspace = _workspace(q.device, nbytes, workspace)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = _lib.load()
     _lib.check(lib.gqa_attention_paged(
         _ptr(q), q.stride(0), q.stride(1), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache),
         k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(page_table),
-        page_table.shape[1], _ptr(kv_len), _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv,
+        max_pages, _ptr(kv_len), _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv,
         d, int(page_size), total_q, int(max_q_len), _scale(scale, d), _ptr(sink),
-        int(bool(causal)), _stream(q.device)))
+        int(bool(causal)), int(tile_s_kv), _ptr(workspace), wsb, _stream(q.device)))
     return out

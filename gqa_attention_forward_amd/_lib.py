@@ -72,7 +72,7 @@ SIGNATURES = {
                                     _I32, _P, _P],
     "gqa_attention_paged": [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P,
                             _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F, _P,
-                            _I32, _P],
+                            _I32, _I32, _P, ctypes.c_size_t, _P],
 }
 
 _lib = None

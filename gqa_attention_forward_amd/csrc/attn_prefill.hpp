@@ -5,8 +5,10 @@
 // commit log, the commit that packs HB = min(G, warps) query heads per
 // block).
 //
-// MFMA mapping, v_mfma_f32_32x32x16_bf16, 32 query rows per wave (the MFMA
-// N dimension):
+// MFMA mapping, v_mfma_f32_32x32x16_bf16, NB blocks of 32 query rows per
+// wave (the MFMA N dimension; with NB = 2 every K and V operand read from
+// LDS feeds two MFMAs, and each block's softmax can overlap the other
+// block's MFMAs inside one wave):
 //   S^T = K Q^T  : A = K rows from LDS, read in a permuted row order (bits 2
 //                  and 3 of the row index swapped) so that accumulator
 //                  registers 8t..8t+7 of a lane hold 8 consecutive keys;
@@ -36,28 +38,29 @@
 
 namespace gqa {
 
-template <int D, int NW>
+template <int D, int NW, int NB>
 struct PrefillCfg {
-  static constexpr bool PP = false;          // ping-pong schedule: measured slower, kept off
-  static constexpr int NSTAGE = PP ? 3 : 2;  // K/V tiles resident in LDS
   static constexpr int BK = 64;              // keys per tile
   static constexpr int DC = D / 8;           // 16-byte chunks per row
   static constexpr int NT = NW * 64;
+  static constexpr int ROWS = 32 * NB * NW;  // query rows per workgroup
   static constexpr int KP = D + 8;           // K row pitch (elements): padded, not swizzled
   static constexpr int KTILE = BK * KP;      // elements of one K tile
   static constexpr int TILE = BK * D;        // elements of one V tile
   static constexpr int STAGE = KTILE + TILE; // K then V
-  static constexpr int LDS_BYTES = NSTAGE * STAGE * 2;
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int CPT = BK * DC / NT;   // chunks per thread per tensor
   static_assert(CPT >= 1 && BK * DC % NT == 0, "tile split");
 };
 
 constexpr float kLazyRescale = 8.f;  // log2 units
 
-template <int D, int NW, bool PAGED, bool PARTIAL>
-__global__ void __launch_bounds__(NW * 64, 2)
+// Two waves per SIMD with one 32-row block per wave; one wave per SIMD (and
+// room for 2x the state) with two.
+template <int D, int NW, int NB, bool PAGED, bool PARTIAL>
+__global__ void __launch_bounds__(NW * 64, NB == 1 ? 2 : 1)
 attn_prefill_kernel(const AttnArgs a) {
-  using C = PrefillCfg<D, NW>;
+  using C = PrefillCfg<D, NW, NB>;
   constexpr int NT = C::NT;
   constexpr int BK = C::BK;
   constexpr int DC = C::DC;
@@ -90,7 +93,7 @@ attn_prefill_kernel(const AttnArgs a) {
   int n = a.Skv;
   if (a.kv_len) n = min(max(a.kv_len[b], 0), a.Skv);
   const int rows_total = q_len * G;
-  const int row0 = qt * (32 * NW);
+  const int row0 = qt * C::ROWS;
   if (row0 >= rows_total) return;
 
   int kbeg = 0, kend = n;
@@ -99,45 +102,46 @@ attn_prefill_kernel(const AttnArgs a) {
     kend = min(n, kbeg + a.tile);
   }
   if (a.causal) {
-    const int p_last = (min(row0 + 32 * NW, rows_total) - 1) / G;
+    const int p_last = (min(row0 + C::ROWS, rows_total) - 1) / G;
     kend = min(kend, min(max(n - q_len + p_last + 1, 0), n));
   }
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-  // ---- this lane's query row and the wave's masking bounds
-  const int rho = row0 + 32 * wv + col;
-  const bool rvalid = rho < rows_total;
-  const int p = rvalid ? rho / G : 0;
-  const int h = g * G + (rvalid ? rho - p * G : 0);
-  int lim = kend;
-  if (a.causal) lim = min(kend, min(max(n - q_len + p + 1, 0), n));
-  const int wrow0 = row0 + 32 * wv;
+  // ---- this lane's query rows (one per 32-row block) and masking bounds
+  const int wrow0 = row0 + 32 * NB * wv;
   int wlo = kend;  // below wlo no row of the wave is masked
   if (a.causal) wlo = min(kend, min(max(n - q_len + wrow0 / G + 1, 0), n));
   if (wrow0 >= rows_total) wlo = kbeg;
-
-  // ---- Q operand: lane holds query row `col`, d = 16 c + 8 hl + e
-  bf16x8 qf[D / 16];
-  {
+  bool rvalid[NB];
+  int pq[NB], hq[NB], lim[NB];
+  bf16x8 qf[NB][D / 16];  // Q operand: row `col` of block nb, d = 16 c + 8 hl + e
+  float sl2[NB], mref[NB], mtrue[NB], l[NB];
+  f32x16 acc[NB][D / 32];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int rho = wrow0 + 32 * nb + col;
+    rvalid[nb] = rho < rows_total;
+    pq[nb] = rvalid[nb] ? rho / G : 0;
+    hq[nb] = g * G + (rvalid[nb] ? rho - pq[nb] * G : 0);
+    lim[nb] = kend;
+    if (a.causal) lim[nb] = min(kend, min(max(n - q_len + pq[nb] + 1, 0), n));
     const uint16_t* qp;
     if constexpr (PAGED)
-      qp = a.q + (int64_t)(q_row0 + p) * a.q_ss + (int64_t)h * a.q_sh;
+      qp = a.q + (int64_t)(q_row0 + pq[nb]) * a.q_ss + (int64_t)hq[nb] * a.q_sh;
     else
-      qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)p * a.q_ss;
+      qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq[nb] * a.q_sh + (int64_t)pq[nb] * a.q_ss;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-      qf[c] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hl) : bf16x8{};
-  }
-
-  float sl2 = -INFINITY;  // sink in log2 units (final mode)
-  if constexpr (!PARTIAL)
-    if (a.sink && rvalid) sl2 = a.sink[h] * kLog2e;
-  float mref = sl2;        // reference the running sums are taken against
-  float mtrue = sl2;       // true running max (for the partial epilogue)
-  float l = 0.f;           // this lane's share of the running sum
-  f32x16 acc[D / 32];
+      qf[nb][c] = rvalid[nb] ? *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hl) : bf16x8{};
+    sl2[nb] = -INFINITY;  // sink in log2 units (final mode)
+    if constexpr (!PARTIAL)
+      if (a.sink && rvalid[nb]) sl2[nb] = a.sink[hq[nb]] * kLog2e;
+    mref[nb] = sl2[nb];   // reference the running sums are taken against
+    mtrue[nb] = sl2[nb];  // true running max (for the partial epilogue)
+    l[nb] = 0.f;          // this lane's share of the running sum
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < D / 32; ++i) acc[nb][i] = f32x16{};
+  }
 
   // ---- K/V staging: chunk ci = tid + i NT of a 64 x DC tile.  Keys at or
   // past kend are never read (loads go to row kend - 1, the keys are masked)
@@ -193,74 +197,93 @@ attn_prefill_kernel(const AttnArgs a) {
   const int krow_a = swap_bits23(col);  // K row (within a 32-key block) this lane feeds to MFMA
   const int g16 = lane >> 4;
   const int r16 = lane & 15;
-  f32x16 s[2];   // S^T of one tile: register j of block mb = key 32 mb + 16 (j >> 3) + 8 hl + (j & 7)
-  bf16x8 pb[4];  // P of one tile as the B operand of four 16-key MFMA steps
-  auto stage_of = [&](int i) -> const uint16_t* { return smem + (i % C::NSTAGE) * C::STAGE; };
 
-  // S^T = K Q^T for tile i (two interleaved accumulation chains), masked
-  auto qk = [&](int i) {
-    const uint16_t* Ks = stage_of(i);
-    const int j0 = kbeg + i * BK;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = kbeg + it * BK;
+    // The prefetch of the next tile is unconditional (past the end it
+    // re-reads the last tile, an L2 hit): with no branch around it the
+    // compiler keeps it ahead of the compute instead of sinking it to its
+    // LDS store.
+    load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
+    const uint16_t* Ks = smem + (it & 1) * C::STAGE;
+    const uint16_t* Vs = Ks + C::KTILE;
+
+    // S^T = K Q^T: register j of s[nb][mb] = key j0 + 32 mb + 16 (j >> 3) + 8 hl + (j & 7)
+    f32x16 s[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb][0] = s[nb][1] = f32x16{};
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const bf16x8 kk = *reinterpret_cast<const bf16x8*>(Ks + (32 * mb + krow_a) * C::KP +
                                                            16 * c + 8 * hl);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qf[c], s[mb], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qf[nb][c], s[nb][mb], 0, 0, 0);
       }
     if (__builtin_expect(j0 + BK > wlo, 0)) {
-      const int rem = lim - j0 - 8 * hl;  // first masked offset of this lane
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int rem = lim[nb] - j0 - 8 * hl;  // first masked offset of this lane
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (32 * mb + 16 * (j >> 3) + (j & 7) >= rem) s[nb][mb][j] = -INFINITY;
+      }
+    }
+
+    // online softmax: tile max, lazy reference move (rare O rescale)
+    float mx[NB];
+    bool move[NB];
+    bool any_move = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float m = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (32 * mb + 16 * (j >> 3) + (j & 7) >= rem) s[mb][j] = -INFINITY;
+        for (int j = 0; j < 16; ++j) m = fmaxf(m, s[nb][mb][j]);
+      mx[nb] = xor32_max(m) * a.scale_log2;
+      mtrue[nb] = fmaxf(mtrue[nb], mx[nb]);
+      move[nb] = mx[nb] > mref[nb] + kLazyRescale;
+      any_move |= move[nb];
     }
-  };
-
-  // online softmax of the tile in s: P -> pb, running (m, l) and the O rescale
-  auto softmax = [&]() {
-    float mx = -INFINITY;
+    if (__any(any_move)) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int nb = 0; nb < NB; ++nb) {
+        const float alpha = move[nb] ? ex2(mref[nb] - mx[nb]) : 1.f;  // 0 when mref = -inf
+        l[nb] *= alpha;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
-    mx = xor32_max(mx) * a.scale_log2;
-    mtrue = fmaxf(mtrue, mx);
-    const bool move = mx > mref + kLazyRescale;
-    if (__any(move)) {
-      const float alpha = move ? ex2(mref - mx) : 1.f;  // 0 when mref = -inf
-      l *= alpha;
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[db][j] *= alpha;
-      mref = move ? mx : mref;
+          for (int j = 0; j < 16; ++j) acc[nb][db][j] *= alpha;
+        mref[nb] = move[nb] ? mx[nb] : mref[nb];
+      }
     }
-    const float mu = (mref == -INFINITY) ? 0.f : mref;
     // P rounded to bf16 in pairs; the row sum is taken over the same rounded
     // values with a packed dot against (1, 1)
-    float ls = 0.f;
+    bf16x8 pb[NB][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int nb = 0; nb < NB; ++nb) {
+      const float mu = (mref[nb] == -INFINITY) ? 0.f : mref[nb];
+      float ls = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        bf16x2 pp;
-        pp[0] = (__bf16)ex2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + e], a.scale_log2, -mu));
-        pp[1] = (__bf16)ex2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + e + 1], a.scale_log2, -mu));
-        pb[t][e] = pp[0];
-        pb[t][e + 1] = pp[1];
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
-      }
-    l += ls;
-  };
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 pp;
+          pp[0] = (__bf16)ex2(__builtin_fmaf(s[nb][t >> 1][8 * (t & 1) + e], a.scale_log2, -mu));
+          pp[1] = (__bf16)ex2(__builtin_fmaf(s[nb][t >> 1][8 * (t & 1) + e + 1], a.scale_log2, -mu));
+          pb[nb][t][e] = pp[0];
+          pb[nb][t][e + 1] = pp[1];
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
+        }
+      l[nb] += ls;
+    }
 
-  // O^T += V^T P^T for tile i
-  auto pv = [&](int i) {
-    const uint16_t* Vs = stage_of(i) + C::KTILE;
+    // O^T += V^T P^T; the V operand is two transposing LDS reads per MFMA
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -277,95 +300,60 @@ attn_prefill_kernel(const AttnArgs a) {
         }
         const bf16x8 vv = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(va[0], va[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[t], acc[db], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[nb][t], acc[nb][db], 0, 0, 0);
       }
     }
-  };
 
-  // The prefetch of the next tile is unconditional (past the end it re-reads
-  // the last tile, an L2 hit): with no branch around it, the compiler keeps
-  // it ahead of the compute instead of sinking it to its LDS store.
-  if constexpr (!C::PP) {
-    for (int it = 0; it < ntiles; ++it) {
-      load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
-      qk(it);
-      softmax();
-      pv(it);
-      store_tile((it + 1) % C::NSTAGE, nx);
-      lds_barrier();
-    }
-  } else {
-    // Ping-pong: waves 0-3 and 4-7 share the four SIMDs pairwise.  Each
-    // iteration has two phases; in each, one group issues its MFMA work
-    // (P.V of the previous tile, then Q.K of this one) while the other runs
-    // the softmax VALU work, so the matrix and vector pipes of a SIMD are fed
-    // by different waves.  Tiles it - 1 (its V) and it (its K) are resident;
-    // tile it + 1 is staged into the third LDS slot.
-    const bool grp_a = wv < 4;
-    constexpr bool PRIO = true;
-    for (int it = 0; it <= ntiles; ++it) {
-      load_tile(kbeg + min(it + 1, max(ntiles - 1, 0)) * BK, nx);
-      if (grp_a) {
-        if (PRIO) __builtin_amdgcn_s_setprio(1);
-        if (it >= 1) pv(it - 1);
-        if (it < ntiles) qk(it);
-        if (PRIO) __builtin_amdgcn_s_setprio(0);
-      } else if (it >= 1) {
-        softmax();  // of tile it - 1, whose S^T this group computed last phase
-      }
-      lds_barrier();
-      if (grp_a) {
-        if (it < ntiles) softmax();
-      } else {
-        if (PRIO) __builtin_amdgcn_s_setprio(1);
-        if (it >= 1) pv(it - 1);
-        if (it < ntiles) qk(it);
-        if (PRIO) __builtin_amdgcn_s_setprio(0);
-      }
-      if (it + 1 < ntiles) store_tile((it + 1) % C::NSTAGE, nx);
-      lds_barrier();
-    }
+    store_tile((it + 1) & 1, nx);
+    lds_barrier();
   }
 
   // ---- epilogue; accumulator register j of d-block db holds
   //      d = 32 db + 8 (j >> 2) + 4 hl + (j & 3) of query row `col`
-  float lt = xor32_sum(l);
-  if constexpr (PARTIAL) {
-    // report the state against the true max (as the partial format states)
-    const float f = (mtrue == -INFINITY) ? 0.f : ex2(mref - mtrue);
-    lt *= f;
-    if (!rvalid) return;
-    int64_t row;
-    if constexpr (PAGED)
-      row = (int64_t)h * a.total_q + q_row0 + p;
-    else
-      row = ((int64_t)b * a.Hq + h) * a.Sq + p;
-    const int64_t idx = row * a.n_split + split;
-    if (hl == 0) a.ws_ml[idx] = make_float2(mtrue == -INFINITY ? -INFINITY : mtrue * kLn2, lt);
-    float* op = a.ws_o + idx * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int nb = 0; nb < NB; ++nb) {
+    float lt = xor32_sum(l[nb]);
+    const int p = pq[nb], h = hq[nb];
+    if constexpr (PARTIAL) {
+      // report the state against the true max (as the partial format states)
+      const float f = (mtrue[nb] == -INFINITY) ? 0.f : ex2(mref[nb] - mtrue[nb]);
+      lt *= f;
+      if (!rvalid[nb]) continue;
+      int64_t row;
+      if constexpr (PAGED)
+        row = (int64_t)h * a.total_q + q_row0 + p;
+      else
+        row = ((int64_t)b * a.Hq + h) * a.Sq + p;
+      const int64_t idx = row * a.n_split + split;
+      if (hl == 0)
+        a.ws_ml[idx] = make_float2(mtrue[nb] == -INFINITY ? -INFINITY : mtrue[nb] * kLn2, lt);
+      float* op = a.ws_o + idx * D;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<float4*>(op + 32 * db + 8 * q4 + 4 * hl) =
-            make_float4(acc[db][4 * q4] * f, acc[db][4 * q4 + 1] * f, acc[db][4 * q4 + 2] * f,
-                        acc[db][4 * q4 + 3] * f);
-  } else {
-    if (sl2 != -INFINITY) lt += ex2(sl2 - mref);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (!rvalid) return;
-    uint16_t* op;
-    if constexpr (PAGED)
-      op = a.o + (int64_t)(q_row0 + p) * a.o_ss + (int64_t)h * a.o_sh;
-    else
-      op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(op + 32 * db + 8 * q4 + 4 * hl) =
+              make_float4(acc[nb][db][4 * q4] * f, acc[nb][db][4 * q4 + 1] * f,
+                          acc[nb][db][4 * q4 + 2] * f, acc[nb][db][4 * q4 + 3] * f);
+    } else {
+      if (sl2[nb] != -INFINITY) lt += ex2(sl2[nb] - mref[nb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (!rvalid[nb]) continue;
+      uint16_t* op;
+      if constexpr (PAGED)
+        op = a.o + (int64_t)(q_row0 + p) * a.o_ss + (int64_t)h * a.o_sh;
+      else
+        op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<uint2*>(op + 32 * db + 8 * q4 + 4 * hl) =
-            make_uint2(pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
-                       pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv));
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<uint2*>(op + 32 * db + 8 * q4 + 4 * hl) =
+              make_uint2(pack_bf16x2(acc[nb][db][4 * q4] * inv, acc[nb][db][4 * q4 + 1] * inv),
+                         pack_bf16x2(acc[nb][db][4 * q4 + 2] * inv, acc[nb][db][4 * q4 + 3] * inv));
+    }
   }
 }
 

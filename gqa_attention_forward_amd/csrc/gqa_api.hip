@@ -120,11 +120,11 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
   return check_launch("attention kernel");
 }
 
-template <int D, int NW, bool PAGED, bool PARTIAL>
+template <int D, int NW, int NB, bool PAGED, bool PARTIAL>
 gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  using C = gqa::PrefillCfg<D, NW>;
-  return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL>, C::LDS_BYTES, C::NT, args,
-                     rows, 32 * NW, stream);
+  using C = gqa::PrefillCfg<D, NW, NB>;
+  return launch_grid(&gqa::attn_prefill_kernel<D, NW, NB, PAGED, PARTIAL>, C::LDS_BYTES, C::NT,
+                     args, rows, C::ROWS, stream);
 }
 
 // Compute units of the current device (queried once per device).
@@ -170,9 +170,11 @@ template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
   if (rows <= 32) return launch_stream<D, 2, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 64) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 128) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
-  return launch_prefill<D, 8, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 64) return launch_prefill<D, 2, 1, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 128) return launch_prefill<D, 4, 1, PAGED, PARTIAL>(args, rows, stream);
+  // 8 waves x 32 rows; the 4 waves x 64 rows form (NB = 2, one wave per
+  // SIMD) measured slower on the causal workload
+  return launch_prefill<D, 8, 1, PAGED, PARTIAL>(args, rows, stream);
 }
 
 template <bool PAGED, bool PARTIAL>
@@ -385,13 +387,16 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
                                  const int32_t* kv_len, void* o, int64_t o_stride_t,
                                  int64_t o_stride_h, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
                                  int32_t page_size, int32_t total_q, int32_t max_q_len,
-                                 float scale, const float* sink, int32_t causal, void* stream) {
+                                 float scale, const float* sink, int32_t causal,
+                                 int32_t tile_s_kv, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   if (B < 0 || total_q < 0 || max_q_len < 0 || max_pages_per_seq < 0)
     return fail(GQA_ERR_INVALID_ARGUMENT, "B, total_q, max_q_len and max_pages_per_seq must be >= 0");
   GQA_TRY(check_heads(Hq, Hkv, d));
   if (page_size != 64) return fail(GQA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", page_size);
   GQA_TRY(check_scale(scale));
   if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  GQA_TRY(check_tile(tile_s_kv, false));
   if (B == 0 || total_q == 0 || max_q_len == 0) return ok();
   GQA_TRY(check_ptr("q", q));
   GQA_TRY(check_ptr("o", o));
@@ -408,6 +413,11 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
   GQA_TRY(check_strides("kv", kvs, 3));
   if ((int64_t)max_pages_per_seq * page_size > 0x7fffffffLL)
     return fail(GQA_ERR_UNSUPPORTED, "max_pages_per_seq too large");
+  const int32_t Skv = max_pages_per_seq * page_size;
+  const int64_t n_split = tile_s_kv > 0 ? (Skv > 0 ? cdiv(Skv, tile_s_kv) : 1) : 1;
+  if (tile_s_kv > 0)
+    GQA_TRY(check_workspace(workspace, workspace_bytes,
+                            workspace_bytes_for((int64_t)Hq * total_q, n_split, d)));
 
   gqa::AttnArgs a{};
   a.q = reinterpret_cast<const uint16_t*>(q);
@@ -419,18 +429,33 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
   a.k_sh = kv_stride_h; a.v_sh = kv_stride_h;
   a.kv_sp = kv_stride_page; a.kv_sr = kv_stride_row;
   a.kv_len = kv_len;
-  a.sink = sink;
   a.cu_seqlens_q = cu_seqlens_q;
   a.page_table = page_table;
   a.max_pages = max_pages_per_seq;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.Sq = max_q_len;
-  a.Skv = max_pages_per_seq * page_size;
+  a.Skv = Skv;
+  a.total_q = total_q;
   a.causal = causal;
-  a.tile = 0;
-  a.n_split = 1;
   a.scale_log2 = scale * gqa::kLog2e;
-  GQA_TRY(dispatch<true, false>(a, d, (int64_t)max_q_len * a.G, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t rows = (int64_t)max_q_len * a.G;
+  if (tile_s_kv == 0) {
+    a.tile = 0;
+    a.n_split = 1;
+    a.sink = sink;
+    GQA_TRY(dispatch<true, false>(a, d, rows, st));
+    return ok();
+  }
+  a.tile = tile_s_kv;
+  a.n_split = (int32_t)n_split;
+  a.ws_ml = reinterpret_cast<float2*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                    (size_t)Hq * total_q * n_split * 8);
+  GQA_TRY(dispatch<true, true>(a, d, rows, st));
+  // partial rows are h * total_q + t: the merge sees B = 1, Sq = total_q
+  const int64_t mo[3] = {0, o_stride_h, o_stride_t};
+  GQA_TRY(launch_merge(workspace, o, mo, 1, Hq, total_q, d, (int32_t)n_split, sink, st));
   return ok();
 }
 

@@ -189,6 +189,12 @@ gqa_status_t gqa_attention_splitkv_merge(const void* workspace, size_t workspace
  *  kv_len       : device int32 [B], required.
  *  page_size    : must be 64.
  *  max_q_len    : host bound on q_len_b that sizes the grid (no device read).
+ *  tile_s_kv    : 0 = one pass per (sequence, kv head, q-tile); > 0 (a
+ *                 multiple of 64) = split-KV over key tiles of that size with
+ *                 partial states in `workspace`, merged by a second kernel.
+ *                 The workspace is gqa_attention_workspace_size(1, Hq,
+ *                 total_q, max_pages_per_seq * page_size, d, tile_s_kv)
+ *                 bytes; partial-state rows are r = h * total_q + t.
  * Page ids are trusted: an id outside the pool is undefined behaviour.
  */
 gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
@@ -200,7 +206,8 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
                                  int64_t o_stride_h, int32_t B, int32_t Hq, int32_t Hkv,
                                  int32_t d, int32_t page_size, int32_t total_q,
                                  int32_t max_q_len, float scale, const float* sink,
-                                 int32_t causal, void* stream);
+                                 int32_t causal, int32_t tile_s_kv, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -71,13 +71,21 @@ int main(void) {
          GQA_ERR_INVALID_ARGUMENT);
 #define PAGED(cu, pt, kvl, page, d, causal) \
   gqa_attention_paged(P, 4096, 128, cu, P, P, 8192, 128, 128, pt, 64, kvl, P, 4096, 128, 8, 32, \
-                      1, d, page, 100, 64, 0.088f, NULL, causal, NULL)
+                      1, d, page, 100, 64, 0.088f, NULL, causal, 0, NULL, 0, NULL)
   expect("paged page 32", PAGED(P, P, P, 32, 128, 0), GQA_ERR_UNSUPPORTED);
   expect("paged NULL cu", PAGED(NULL, P, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("paged NULL table", PAGED(P, NULL, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("paged NULL kv_len", PAGED(P, P, NULL, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("paged d 256", PAGED(P, P, P, 64, 256, 0), GQA_ERR_UNSUPPORTED);
   expect("paged causal 3", PAGED(P, P, P, 64, 128, 3), GQA_ERR_INVALID_ARGUMENT);
+  expect("paged split, no workspace",
+         gqa_attention_paged(P, 4096, 128, P, P, P, 8192, 128, 128, P, 64, P, P, 4096, 128, 8, 32,
+                             1, 128, 64, 100, 64, 0.088f, NULL, 0, 512, NULL, 0, NULL),
+         GQA_ERR_WORKSPACE);
+  expect("paged tile 100",
+         gqa_attention_paged(P, 4096, 128, P, P, P, 8192, 128, 128, P, 64, P, P, 4096, 128, 8, 32,
+                             1, 128, 64, 100, 64, 0.088f, NULL, 0, 100, P, 1 << 30, NULL),
+         GQA_ERR_INVALID_ARGUMENT);
   printf("%s\n", failures ? "FAILED" : "ALL OK");
   return failures ? 1 : 0;
 }

@@ -117,18 +117,57 @@ def test_shortq_longkv_one_pass_equals_split():
     assert np.abs(a - b).max() <= 2 * 2.0 ** -8 * np.abs(a).max() + 1e-6
 
 
-def test_ragged_paged_full():
-    note("ragged paged workload (B=8, Hq=32, Hkv=1, NaN padding, sink)")
-    w = workloads.make_paged()
-    g = to_dev(w)
-    out = gqa().paged(g["q"], g["cu_seqlens_q"], g["k_cache"], g["v_cache"], g["page_table"],
-                      g["kv_len"], max_q_len=w["max_q_len"], scale=w["scale"], sink=g["sink"])
-    torch.cuda.synchronize()
-    want = oracle.paged_attention_fp64(to_f64(w["q"]), w["cu_seqlens_q"].numpy(),
+def _paged_oracle(w, causal=False):
+    return oracle.paged_attention_fp64(to_f64(w["q"]), w["cu_seqlens_q"].numpy(),
                                        to_f64(w["k_cache"]), to_f64(w["v_cache"]),
                                        w["page_table"].numpy(), w["kv_len"].numpy(),
-                                       scale=w["scale"], page_size=64, sink=to_f64(w["sink"]))
-    assert_close(out.float().cpu().numpy(), want, "paged")
+                                       scale=w["scale"], page_size=64,
+                                       sink=None if w["sink"] is None else to_f64(w["sink"]),
+                                       causal=causal)
+
+
+def _paged_run(w, causal=False, tile=0):
+    g = to_dev(w)
+    out = gqa().paged(g["q"], g["cu_seqlens_q"], g["k_cache"], g["v_cache"], g["page_table"],
+                      g["kv_len"], max_q_len=w["max_q_len"], scale=w["scale"], sink=g["sink"],
+                      causal=causal, tile_s_kv=tile)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("tile", [0, 512, 64])
+def test_ragged_paged_full(tile):
+    note(f"ragged paged workload (B=8, Hq=32, Hkv=1, NaN padding, sink), tile={tile}")
+    w = workloads.make_paged()
+    assert_close(_paged_run(w, tile=tile), _paged_oracle(w), f"paged tile={tile}")
+
+
+@pytest.mark.parametrize("tile", [0, 256])
+def test_paged_causal_chunked_prefill(tile):
+    """Chunked prefill over a cached prefix: q_len <= kv_len, bottom-right causal."""
+    note(f"paged causal chunked prefill tile={tile}")
+    w = workloads.make_paged(B=5, Hq=16, Hkv=4, d=128, q_lens=[7, 64, 1, 33, 100],
+                             kv_lens=[300, 64, 1000, 40, 777], seed=21)
+    assert_close(_paged_run(w, causal=True, tile=tile), _paged_oracle(w, causal=True),
+                 f"paged causal tile={tile}")
+
+
+@pytest.mark.parametrize("G", [4, 32])
+@pytest.mark.parametrize("tile", [0, 1024])
+def test_paged_decode_shape(G, tile):
+    """One query token per sequence (the stream kernel's paged path)."""
+    note(f"paged decode G={G} tile={tile}")
+    w = workloads.make_paged(B=6, Hq=32, Hkv=32 // G, d=128, q_lens=[1] * 6,
+                             kv_lens=[1, 63, 64, 65, 2000, 4096], seed=22 + G)
+    assert_close(_paged_run(w, tile=tile), _paged_oracle(w), f"paged decode G={G} tile={tile}")
+
+
+def test_paged_d64():
+    note("paged d=64 ragged")
+    w = workloads.make_paged(B=3, Hq=8, Hkv=2, d=64, q_lens=[5, 40, 17], kv_lens=[100, 3, 640],
+                             seed=23)
+    assert_close(_paged_run(w, tile=0), _paged_oracle(w), "paged d64")
+    assert_close(_paged_run(w, tile=128), _paged_oracle(w), "paged d64 split")
 
 
 # ---------------------------------------------------------------- small sweeps

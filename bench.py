@@ -184,14 +184,14 @@ def bench_secondary(args, device, stream):
         "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2), "flops": fl,
         "roofline": roof("mfma", fl / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s")}
     del g, out
-    # ragged paged with sink: one pass and split-KV (tiles of 512 keys)
+    # ragged paged with sink: one pass and split-KV (tiles of 1024 keys)
     w = workloads.make_paged()
     gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
     m = gqa()
     outp = torch.empty_like(gw["q"])
     pb, pf = paged_work(w)
     t_roof = max(pb / (HBM_PEAK_GBS * 1e9), pf / (BF16_PEAK_TFLOPS * 1e12))
-    for tile in (0, 512):
+    for tile in (0, 1024):
         ws = None
         if tile:
             ws = torch.empty(m.workspace_size(1, w["Hq"], w["total_q"],
@@ -233,7 +233,7 @@ def run_only(args, device, stream):
         m = gqa()
         fn = lambda: m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],  # noqa: E731
                              gw["page_table"], gw["kv_len"], max_q_len=w["max_q_len"],
-                             scale=w["scale"], sink=gw["sink"], tile_s_kv=512)
+                             scale=w["scale"], sink=gw["sink"], tile_s_kv=1024)
         return {"workload": name, "ms": time_loop(fn, args.steps, args.warmup, stream)}
     c, _, g = setup_dense(name, device)
     step, _ = prefill_step_fn(g, c, 2048 if name == "shortq_longkv" else 0)

@@ -69,7 +69,7 @@ attn_prefill_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31;
   const int hl = lane >> 5;
 

@@ -1,14 +1,17 @@
 // Stream GQA forward kernel for query groups of at most 16 * NQB rows per
 // (b, kv head): single-token decode and short query blocks.
 //
-// Each workgroup owns one (b, kv head g, q-tile, kv split).  Its NW waves
-// split the split's keys into 32-key tiles taken round-robin, and each wave
-// streams its tiles on its own: there is no workgroup barrier inside the key
-// loop.  A wave keeps the next tile's K and V in flight in registers while it
-// computes on the current one.  The waves' running states (m, l, O) are
-// combined through LDS at the end (the associative (m, l, O) merge of the
-// kernbench2 2-D mesh all-reduce-mlo commit), then written as one split
-// partial or as the final normalised output.
+// Each workgroup owns one (b, kv head g, q-tile) and a run of `spw`
+// consecutive kv splits.  Its NW waves cut the run's keys into 32-key tiles
+// taken round-robin, and each wave streams its tiles on its own.  A wave
+// keeps the next tile's K and V in flight in registers while it computes on
+// the current one.  When a wave's next tile belongs to a later split, the
+// waves' running states (m, l, O) are combined through LDS (the associative
+// (m, l, O) merge of the kernbench2 2-D mesh all-reduce-mlo commit) and
+// written as that split's partial (or as the final normalised output when
+// there is no split); the prefetched tile stays in flight meanwhile.  Longer
+// runs per workgroup stream HBM faster than one split each (fewer, longer
+// sequential streams), while the partials keep the split size.
 //
 // MFMA mapping, v_mfma_f32_16x16x32_bf16 (16 query columns per block, so a
 // 4-row GQA group wastes 12 columns instead of 28 with the 32-wide form):
@@ -39,15 +42,27 @@ struct StreamCfg {
   static constexpr int VPL = BK * DC / 64;  // V chunks per lane per tile
   static constexpr int VTILE = BK * D;      // V tile elements (per wave)
   static constexpr int SLOT_F = NQB * (2 + 4 * NDB) * 64;  // combine floats per wave
-  static constexpr int WAVE_BYTES = (VTILE * 2 > SLOT_F * 4 ? VTILE * 2 : SLOT_F * 4);
+  static constexpr int PSTR = D + 4;       // parked column: O (D floats), m, l, pad
+  static constexpr int PEND_F = NQB * 16 * PSTR;  // parked floats per split
+  static constexpr int MAX_SPW = NQB == 1 ? 8 : 4;  // splits per workgroup (LDS bound)
+  // LDS: one V tile per wave, one combine slot per wave other than 0, and
+  // (partial mode) one parked state per split of the run
+  static constexpr int lds_bytes(int nw, int spw) {
+    return nw * VTILE * 2 + (nw - 1) * SLOT_F * 4 + spw * PEND_F * 4;
+  }
 };
 
-// Two waves per SIMD for one 16-column block; one for two blocks (the second
-// block's Q, S and O would not fit two waves' register budget).
+// One wave per SIMD: the register budget then holds two in-flight tiles,
+// Q, O and the softmax state without spilling (a spill reload waits behind
+// the tile loads in flight), and this HBM-bound kernel streams fastest with
+// few, long-running waves per CU anyway.
 template <int D, int NQB, int NW, bool PAGED, bool PARTIAL>
-__global__ void __launch_bounds__(NW * 64, NQB == 1 ? 2 : 1)
+__global__ void __launch_bounds__(NW * 64, 1)
 attn_stream_kernel(const AttnArgs a) {
   using C = StreamCfg<D, NQB>;
+  // tiles in flight per wave while it computes on one (a deeper rotation
+  // measured no faster and needs one wave per SIMD)
+  constexpr int DEPTH = 1;
   constexpr int BK = C::BK;
   constexpr int NC = C::NC;
   constexpr int NDB = C::NDB;
@@ -56,7 +71,9 @@ attn_stream_kernel(const AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  // wave index, made visibly wave-uniform so loops over a wave's tiles are
+  // scalar loops (a divergent loop makes the compiler wait on in-flight loads)
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -64,8 +81,11 @@ attn_stream_kernel(const AttnArgs a) {
   const int nbg = a.B * a.Hkv;
   const int bg = L % nbg;
   const int rest = L / nbg;
-  const int split = rest % a.n_split;
-  const int qt = a.n_qtiles - 1 - rest / a.n_split;
+  const int n_sg = (a.n_split + a.spw - 1) / a.spw;
+  const int sg = rest % n_sg;
+  const int qt = a.n_qtiles - 1 - rest / n_sg;
+  const int s0 = sg * a.spw;                   // first split of the run
+  const int nsp = min(a.spw, a.n_split - s0);  // splits in the run
   const int b = bg / a.Hkv;
   const int g = bg % a.Hkv;
   const int G = a.G;
@@ -85,8 +105,8 @@ attn_stream_kernel(const AttnArgs a) {
 
   int kbeg = 0, kend = n;
   if (a.tile > 0) {
-    kbeg = split * a.tile;
-    kend = min(n, kbeg + a.tile);
+    kbeg = s0 * a.tile;
+    kend = min(n, kbeg + nsp * a.tile);
   }
   if (a.causal) {
     const int p_last = (min(row0 + 16 * NQB, rows_total) - 1) / G;
@@ -132,48 +152,55 @@ attn_stream_kernel(const AttnArgs a) {
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{};
   }
 
-  auto krow = [&](int key) -> const uint16_t* {
-    if constexpr (PAGED) {
-      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
-      return a.k + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.k_sh;
-    } else {
-      return a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)key * a.k_ss;
-    }
-  };
-  auto vrow = [&](int key) -> const uint16_t* {
-    if constexpr (PAGED) {
-      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
-      return a.v + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.v_sh;
-    } else {
-      return a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)key * a.v_ss;
-    }
-  };
-
-  // one tile in registers: K in MFMA A layout, V as row chunks.  Keys at or
-  // past kend are never read: their loads are redirected to row kend - 1
-  // (real, finite data) and the keys are masked below, so they get P = 0
-  // exactly.  Branch-free loads keep the compiler's wait counts exact, which
-  // is what lets the next tile's loads stay in flight during this tile's math.
+  // one tile in registers: K in MFMA A layout, V as row chunks.  A tile's
+  // 32 rows are loaded through a buffer resource whose size ends at the
+  // tile's last row before kv_len (a 32-key tile never straddles a 64-key
+  // page), so rows past kv_len read as zeros without touching memory, and
+  // keys at or past kend are masked below (P = 0 exactly): whatever such rows
+  // hold never reaches the output.  Each lane's offsets are constants; the
+  // tile start and its page are wave-uniform scalar work.  Branch-free loads
+  // keep the compiler's wait counts exact, which is what lets the next tile's
+  // loads stay in flight during this tile's math.
   struct Tile {
     uint4 k[2][NC];
     uint4 v[VPL];
   };
-  const int klast = kend - 1;
+  const uint32_t kss2 = (uint32_t)(PAGED ? a.kv_sr : a.k_ss) * 2u;
+  const uint32_t vss2 = (uint32_t)(PAGED ? a.kv_sr : a.v_ss) * 2u;
+  uint32_t koff[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) koff[kb] = (uint32_t)(16 * kb + c16) * kss2 + 16u * grp;
+  const uint32_t voff = (uint32_t)(lane / DC) * vss2 + 16u * (lane % DC);
+  const uint32_t vstep = (uint32_t)(64 / DC) * vss2;
+  // page table through the constant address space: uniform reads become
+  // scalar loads, which do not queue behind the tile loads in flight
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)a.page_table;
   auto load = [&](int j0, Tile& t) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint16_t* r = krow(min(j0 + 16 * kb + c16, klast));
-#pragma unroll
-      for (int c = 0; c < NC; ++c) t.k[kb][c] = *reinterpret_cast<const uint4*>(r + 32 * c + 8 * grp);
+    const uint16_t *kp, *vp;
+    if constexpr (PAGED) {
+      const int pg = ptab[(int64_t)b * a.max_pages + (j0 >> 6)];
+      const int64_t off = (int64_t)pg * a.kv_sp + (int64_t)(j0 & 63) * a.kv_sr;
+      kp = a.k + off + (int64_t)g * a.k_sh;
+      vp = a.v + off + (int64_t)g * a.v_sh;
+    } else {
+      kp = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)j0 * a.k_ss;
+      vp = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)j0 * a.v_ss;
     }
+    const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
+    const BufRes kr = make_bufres(kp, (valid - 1u) * kss2 + (uint32_t)D * 2u);
+    const BufRes vr = make_bufres(vp, (valid - 1u) * vss2 + (uint32_t)D * 2u);
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int ci = lane + 64 * j;
-      t.v[j] = *reinterpret_cast<const uint4*>(vrow(min(j0 + ci / DC, klast)) + 8 * (ci % DC));
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16(kr, koff[kb] + 64u * c);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16(vr, voff + (uint32_t)j * vstep);
   };
 
-  uint16_t* vbuf = smem + wv * (C::WAVE_BYTES / 2);
+  uint16_t* vbuf = smem + wv * C::VTILE;
+  float* slots = reinterpret_cast<float*>(smem + NW * C::VTILE);
+  float* pend = slots + (NW - 1) * C::SLOT_F;  // parked split states (partial mode)
 
   auto compute = [&](int j0, const Tile& t) {
     // V tile -> wave-private LDS (row-major, swizzled 16-byte slots)
@@ -249,103 +276,173 @@ attn_stream_kernel(const AttnArgs a) {
     }
   };
 
-  // ---- key loop: this wave takes tiles wv, wv + NW, ...; two register tiles
-  // in rotation.  The prefetch is unconditional (past the end it re-reads the
-  // wave's last tile, which is still in L2) so no branch sits between a load
-  // and the compute that must not wait for it.
+  // ---- end of a split: combine the NW waves' states through LDS (wave 0
+  // keeps the result), write the split's partial or the final output, and
+  // start the next split from the empty state.  Every wave calls this once
+  // per split of the run, in order, so the barriers match.
+  auto flush = [&](int s) __attribute__((always_inline)) {
+    if constexpr (NW > 1) {
+      if (s > 0) lds_barrier();  // wave 0 has read the previous split's slots
+      if (wv > 0) {
+        float* red = slots + (wv - 1) * C::SLOT_F;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float* r = red + qb * (2 + 4 * NDB) * 64;
+          r[lane] = m[qb];
+          r[64 + lane] = l[qb];
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[(2 + 4 * db + e) * 64 + lane] = acc[qb][db][e];
+        }
+      }
+      lds_barrier();
+      if (wv == 0) {
+#pragma unroll 1
+        for (int w2 = 1; w2 < NW; ++w2) {
+          const float* base = slots + (w2 - 1) * C::SLOT_F;
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float* r = base + qb * (2 + 4 * NDB) * 64;
+            const float m2 = r[lane];
+            const float l2 = r[64 + lane];
+            const float mn = fmaxf(m[qb], m2);
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            const float wa = ex2(m[qb] - mu);
+            const float wb = ex2(m2 - mu);
+            l[qb] = l[qb] * wa + l2 * wb;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[qb][db][e] = acc[qb][db][e] * wa + r[(2 + 4 * db + e) * 64 + lane] * wb;
+            m[qb] = mn;
+          }
+        }
+      }
+    }
+    // epilogue (wave 0); acc[qb][db][e] holds d = 16 db + 4 grp + e of column c16
+    if (wv == 0) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float lt = l[qb];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (!rvalid[qb]) continue;
+        const int p = pq[qb], h = hq[qb];
+        if constexpr (PARTIAL) {
+          // park the split's state in LDS; it is written out after the loop
+          float* pc = pend + ((s * NQB + qb) * 16 + c16) * C::PSTR;
+          if (grp == 0)
+            *reinterpret_cast<float2*>(pc + D) =
+                make_float2(m[qb] == -INFINITY ? -INFINITY : m[qb] * kLn2, lt);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            *reinterpret_cast<float4*>(pc + 16 * db + 4 * grp) =
+                make_float4(acc[qb][db][0], acc[qb][db][1], acc[qb][db][2], acc[qb][db][3]);
+        } else {
+          float sl2 = -INFINITY;
+          if (a.sink) sl2 = a.sink[h] * kLog2e;
+          if (sl2 != -INFINITY) lt += ex2(sl2 - m[qb]);
+          const float inv = lt > 0.f ? 1.f / lt : 0.f;
+          uint16_t* op;
+          if constexpr (PAGED)
+            op = a.o + (int64_t)(q_row0 + p) * a.o_ss + (int64_t)h * a.o_sh;
+          else
+            op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp) =
+                make_uint2(pack_bf16x2(acc[qb][db][0] * inv, acc[qb][db][1] * inv),
+                           pack_bf16x2(acc[qb][db][2] * inv, acc[qb][db][3] * inv));
+        }
+      }
+    }
+    if constexpr (PARTIAL) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{};
+      }
+    }
+  };
+
+  // ---- key loop: this wave takes tiles wv, wv + NW, ... of the run;
+  // DEPTH + 1 register tiles in rotation.  The prefetch is unconditional
+  // (past the end it re-reads the wave's last tile, which is still in L2) so
+  // no branch sits between a load and the compute that must not wait for it.
+  // Splits are multiples of 64 keys, so no tile straddles two of them.  The
+  // finished splits are flushed before the first tile of a later split, at a
+  // point where that tile (and the DEPTH - 1 after it) is in flight and the
+  // remaining register tile is free.
   {
+    const int tps = a.tile > 0 ? a.tile / BK : 0x7fffffff;  // tiles per split
+    int cur = 0;                 // split (within the run) being accumulated
+    int next_tile = tps;         // first tile of split cur + 1
+    auto enter = [&](int k) __attribute__((always_inline)) {
+      const int t = wv + NW * k;
+      while (t >= next_tile) {
+        flush(cur);
+        ++cur;
+        next_tile += tps;
+      }
+    };
     const int mine = wv < ntiles ? (ntiles - wv + NW - 1) / NW : 0;
     auto tile_key = [&](int k) { return kbeg + (wv + NW * min(k, mine - 1)) * BK; };
     if (mine > 0) {
-      Tile t0, t1;
-      load(tile_key(0), t0);
-      for (int k = 0; k < mine; k += 2) {
-        load(tile_key(k + 1), t1);
-        compute(tile_key(k), t0);
-        if (k + 1 >= mine) break;
-        load(tile_key(k + 2), t0);
-        compute(tile_key(k + 1), t1);
+      Tile t[DEPTH + 1];
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) load(tile_key(u), t[u]);
+      // The exit leaves both loops at once: a path back through the loop
+      // head with a prefetched tile left unconsumed would make the compiler
+      // wait for that tile on every iteration.
+      for (int k = 0;; k += DEPTH + 1) {
+#pragma unroll
+        for (int u = 0; u <= DEPTH; ++u) {
+          if (k + u >= mine) goto keys_done;
+          enter(k + u);
+          load(tile_key(k + u + DEPTH), t[(u + DEPTH) % (DEPTH + 1)]);
+          // keep the prefetch ahead of the first wait on tile k + u
+          __builtin_amdgcn_sched_barrier(0);
+          compute(tile_key(k + u), t[u]);
+        }
       }
+    }
+  keys_done:
+    while (cur < nsp) {
+      flush(cur);
+      ++cur;
     }
   }
 
-  // ---- combine the NW waves' states through LDS (wave 0 keeps the result)
-  if constexpr (NW > 1) {
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(smem) + wv * (C::WAVE_BYTES / 4);
-    if (wv > 0) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float* r = red + qb * (2 + 4 * NDB) * 64;
-        r[lane] = m[qb];
-        r[64 + lane] = l[qb];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[(2 + 4 * db + e) * 64 + lane] = acc[qb][db][e];
-      }
-    }
-    __syncthreads();
-    if (wv != 0) return;
-#pragma unroll
-    for (int w2 = 1; w2 < NW; ++w2) {
-      const float* base = reinterpret_cast<const float*>(smem) + w2 * (C::WAVE_BYTES / 4);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float* r = base + qb * (2 + 4 * NDB) * 64;
-        const float m2 = r[lane];
-        const float l2 = r[64 + lane];
-        const float mn = fmaxf(m[qb], m2);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float wa = ex2(m[qb] - mu);
-        const float wb = ex2(m2 - mu);
-        l[qb] = l[qb] * wa + l2 * wb;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[qb][db][e] = acc[qb][db][e] * wa + r[(2 + 4 * db + e) * 64 + lane] * wb;
-        m[qb] = mn;
-      }
-    }
-  }
-
-  // ---- epilogue; acc[qb][db][e] holds d = 16 db + 4 grp + e of column c16
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    float lt = l[qb];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    if (!rvalid[qb]) continue;
-    const int p = pq[qb], h = hq[qb];
-    if constexpr (PARTIAL) {
+  // ---- split partials: the run's parked states go out with coalesced
+  // stores, two query columns per wave instruction.  Global stores stay out
+  // of the key loop, where the registers they read would have to be guarded
+  // by waits that also hold back the prefetch.
+  if constexpr (PARTIAL) {
+    lds_barrier();
+    constexpr int LPC = D / 4;  // lanes per column (float4 each)
+    const int half = lane >> 5, ln = lane & 31;
+    for (int it = 2 * wv + half; it < nsp * NQB * 16; it += 2 * NW) {
+      const int s = it / (NQB * 16);
+      const int qb = (it / 16) % NQB;
+      const int col = it % 16;
+      const int rho = row0 + 16 * qb + col;
+      if (rho >= rows_total) continue;
+      const int p = rho / G, h = g * G + (rho - p * G);
       int64_t row;
       if constexpr (PAGED)
         row = (int64_t)h * a.total_q + q_row0 + p;
       else
         row = ((int64_t)b * a.Hq + h) * a.Sq + p;
-      const int64_t idx = row * a.n_split + split;
-      if (grp == 0) a.ws_ml[idx] = make_float2(m[qb] == -INFINITY ? -INFINITY : m[qb] * kLn2, lt);
-      float* op = a.ws_o + idx * D + 4 * grp;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        *reinterpret_cast<float4*>(op + 16 * db) =
-            make_float4(acc[qb][db][0], acc[qb][db][1], acc[qb][db][2], acc[qb][db][3]);
-    } else {
-      float sl2 = -INFINITY;
-      if (a.sink) sl2 = a.sink[h] * kLog2e;
-      if (sl2 != -INFINITY) lt += ex2(sl2 - m[qb]);
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* op;
-      if constexpr (PAGED)
-        op = a.o + (int64_t)(q_row0 + p) * a.o_ss + (int64_t)h * a.o_sh;
-      else
-        op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        *reinterpret_cast<uint2*>(op + 16 * db + 4 * grp) =
-            make_uint2(pack_bf16x2(acc[qb][db][0] * inv, acc[qb][db][1] * inv),
-                       pack_bf16x2(acc[qb][db][2] * inv, acc[qb][db][3] * inv));
+      const int64_t idx = row * a.n_split + s0 + s;
+      const float* pc = pend + ((s * NQB + qb) * 16 + col) * C::PSTR;
+      if (ln < LPC)
+        *reinterpret_cast<float4*>(a.ws_o + idx * D + 4 * ln) =
+            *reinterpret_cast<const float4*>(pc + 4 * ln);
+      if (ln == 0) a.ws_ml[idx] = *reinterpret_cast<const float2*>(pc + D);
     }
   }
 }

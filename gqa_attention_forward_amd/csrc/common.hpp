@@ -68,10 +68,23 @@ struct AttnArgs {
   int32_t causal;
   int32_t tile;       // keys per split (0 = the whole range)
   int32_t n_split;
+  int32_t spw;        // consecutive splits per workgroup (stream kernel; 1 elsewhere)
   int32_t n_qtiles;   // q-tiles per (b, g)
   int32_t total_q;    // paged: packed query rows (partial-state row = h * total_q + t)
   float scale_log2;   // scale * log2(e), > 0
 };
+
+// Raw buffer resource (CDNA: stride 0, no swizzle, third dword 0x00020000).
+// Loads at offsets at or past `bytes` return zeros without touching memory.
+using BufRes = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ BufRes make_bufres(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(BufRes r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);

@@ -94,7 +94,8 @@ gqa_status_t check_launch(const char* what) {
 // grid; `rows_per_tile` query rows of a kv group per workgroup.
 template <class K>
 gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args,
-                         int64_t q_rows_per_bg, int rows_per_tile, hipStream_t stream) {
+                         int64_t q_rows_per_bg, int rows_per_tile, hipStream_t stream,
+                         int lds_max = 0) {
   // dynamic LDS above 64 KiB has to be allowed once per kernel; the cache
   // is keyed by the kernel address
   static std::mutex mu;
@@ -106,13 +107,15 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
     for (int i = 0; i < ndone; ++i) seen |= done[i] == reinterpret_cast<const void*>(kern);
     if (!seen) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         lds_max > lds_bytes ? lds_max : lds_bytes);
       if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
       if (ndone < 64) done[ndone++] = reinterpret_cast<const void*>(kern);
     }
   }
   args.n_qtiles = (int32_t)cdiv(q_rows_per_bg, rows_per_tile);
-  const int64_t nblocks = (int64_t)args.B * args.Hkv * args.n_split * args.n_qtiles;
+  if (args.spw < 1) args.spw = 1;
+  const int64_t nblocks = (int64_t)args.B * args.Hkv * cdiv(args.n_split, args.spw) * args.n_qtiles;
   if (nblocks <= 0) return GQA_OK;
   if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large (%lld)", (long long)nblocks);
   (void)hipGetLastError();  // clear a stale error so the check below is ours
@@ -123,6 +126,7 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
 template <int D, int NW, int NB, bool PAGED, bool PARTIAL>
 gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   using C = gqa::PrefillCfg<D, NW, NB>;
+  args.spw = 1;
   return launch_grid(&gqa::attn_prefill_kernel<D, NW, NB, PAGED, PARTIAL>, C::LDS_BYTES, C::NT,
                      args, rows, C::ROWS, stream);
 }
@@ -146,20 +150,30 @@ int device_cus() {
 template <int D, int NQB, int NW, bool PAGED, bool PARTIAL>
 gqa_status_t launch_stream_nw(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   using C = gqa::StreamCfg<D, NQB>;
-  return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL>, NW * C::WAVE_BYTES,
-                     NW * 64, args, rows, 16 * NQB, stream);
+  return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL>,
+                     C::lds_bytes(NW, PARTIAL ? args.spw : 0), NW * 64, args, rows, 16 * NQB,
+                     stream, C::lds_bytes(NW, PARTIAL ? C::MAX_SPW : 0));
 }
 
-// Waves per workgroup: the most waves that still let every workgroup be
-// resident at once (8 waves per CU at two waves per SIMD), so no workgroup
-// waits for a second round; 4 when even that does not fit.
+// Launch shape of the stream kernel.  Split-KV runs: each workgroup takes
+// `spw` consecutive splits, as many as still leave at least one workgroup
+// per CU: HBM streams faster with fewer, longer sequential runs (measured on
+// the 16 x 8-head x 8-split decode: 1 split per workgroup 98-99 us, 2 or 4
+// splits 95-96 us).  Two waves per workgroup once there are at least as
+// many workgroups as CUs (the same decode: 2 waves per workgroup beat 4);
+// four when the grid is smaller, to use more of each CU.
 template <int D, int NQB, bool PAGED, bool PARTIAL>
 gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  const int64_t nblocks = (int64_t)args.B * args.Hkv * args.n_split * cdiv(rows, 16 * NQB);
-  const int64_t waves_per_cu = NQB == 1 ? 8 : 4;
-  const int64_t slots = (int64_t)device_cus() * waves_per_cu;
-  if (nblocks * 4 <= slots || nblocks * 2 > slots)
-    return launch_stream_nw<D, NQB, 4, PAGED, PARTIAL>(args, rows, stream);
+  const int64_t cus = device_cus();
+  const int64_t per_split = (int64_t)args.B * args.Hkv * cdiv(rows, 16 * NQB);
+  int spw = 1;
+  if (PARTIAL)
+    while (spw * 2 <= gqa::StreamCfg<D, NQB>::MAX_SPW && spw * 2 <= args.n_split &&
+           per_split * cdiv(args.n_split, spw * 2) >= cus)
+      spw *= 2;
+  args.spw = spw;
+  const int64_t nblocks = per_split * cdiv(args.n_split, spw);
+  if (nblocks < cus) return launch_stream_nw<D, NQB, 4, PAGED, PARTIAL>(args, rows, stream);
   return launch_stream_nw<D, NQB, 2, PAGED, PARTIAL>(args, rows, stream);
 }
 

@@ -240,6 +240,15 @@ gqa::AttnArgs dense_args(const void* q, const int64_t* qs, const void* k, const 
 }
 
 // Shared checks of the dense entry points.
+// K/V tiles are read through buffer resources with 32-bit offsets spanning
+// 32 key rows; this bound keeps every offset in range.
+gqa_status_t check_key_stride(const char* name, int64_t st) {
+  if (st >= (int64_t)1 << 26)
+    return fail(GQA_ERR_UNSUPPORTED, "%s key-row stride (%lld) must be below 2^26 elements", name,
+                (long long)st);
+  return GQA_OK;
+}
+
 gqa_status_t check_dense(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
                          const void* v, const int64_t* vs, int32_t B, int32_t Hq, int32_t Hkv,
                          int32_t Sq, int32_t Skv, int32_t d, float scale, int32_t causal) {
@@ -255,6 +264,8 @@ gqa_status_t check_dense(const void* q, const int64_t* qs, const void* k, const 
   GQA_TRY(check_strides("q", qs, 3));
   GQA_TRY(check_strides("k", ks, 3));
   GQA_TRY(check_strides("v", vs, 3));
+  GQA_TRY(check_key_stride("k", ks[2]));
+  GQA_TRY(check_key_stride("v", vs[2]));
   return GQA_OK;
 }
 
@@ -425,6 +436,7 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
   GQA_TRY(check_strides("q", qs, 2));
   GQA_TRY(check_strides("o", os, 2));
   GQA_TRY(check_strides("kv", kvs, 3));
+  GQA_TRY(check_key_stride("kv", kv_stride_row));
   if ((int64_t)max_pages_per_seq * page_size > 0x7fffffffLL)
     return fail(GQA_ERR_UNSUPPORTED, "max_pages_per_seq too large");
   const int32_t Skv = max_pages_per_seq * page_size;

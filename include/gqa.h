@@ -47,7 +47,9 @@
  *    max_q_len == 0) is a no-op that returns GQA_OK after the scalar checks;
  *    its pointers are not examined and may be NULL.
  *  - Base pointers must be 16-byte aligned and the (b, h, s) strides of
- *    bf16 tensors multiples of 8 elements, else GQA_ERR_UNSUPPORTED.
+ *    bf16 tensors multiples of 8 elements, else GQA_ERR_UNSUPPORTED.  The
+ *    stride between consecutive key rows of K and V (dense s stride, paged
+ *    kv_stride_row) must be below 2^26 elements, else GQA_ERR_UNSUPPORTED.
  *    d must be 64 or 128, else GQA_ERR_UNSUPPORTED.
  *
  * Ownership: the caller owns all memory and keeps it alive until the work

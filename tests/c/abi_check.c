@@ -41,6 +41,19 @@ int main(void) {
   expect("misaligned q", PREFILL(M, s, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
   expect("stride not x8", PREFILL(P, bad, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
   expect("NULL strides", PREFILL(P, NULL, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
+  {
+    const int64_t huge[3] = {(int64_t)1 << 40, (int64_t)1 << 34, (int64_t)1 << 26};
+    expect("k row stride 2^26",
+           gqa_attention_prefill(P, s, P, huge, P, s, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
+                                 NULL, 0, 0, NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+    expect("v row stride 2^26",
+           gqa_attention_prefill(P, s, P, s, P, huge, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
+                                 NULL, 0, 0, NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+    expect("paged row stride 2^26",
+           gqa_attention_paged(P, 4096, 128, P, P, P, (int64_t)1 << 33, (int64_t)1 << 26, 128, P,
+                               64, P, P, 4096, 128, 8, 32, 1, 128, 64, 100, 64, 0.088f, NULL, 0, 0,
+                               NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+  }
   expect("d = 96", PREFILL(P, s, 96, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
   expect("Hq % Hkv", PREFILL(P, s, 64, 6, 4, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("Hkv = 0", PREFILL(P, s, 64, 4, 0, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);

@@ -10,7 +10,10 @@ kernel); `value` is its K/V-stream throughput in GB/s of algorithmic bytes
 
 * roofline: the dominant kernel (the split-KV partial kernel) timed alone
   with HIP events on its own stream, algorithmic bytes per launch over its
-  mean duration, against MI355X's 8 TB/s HBM peak;
+  mean duration, against MI355X's 8 TB/s HBM peak; `traffic` is the HBM
+  bytes per launch from the committed counter summary
+  (profiles/decode_partial_hbm_traffic.txt), null once the kernel sources
+  differ from the ones it was measured on;
 * secondary: the other named workloads (short-q/long-kv prefill, causal
   prefill, ragged paged, tiny prefill), each timed the same way with its own
   roofline fraction;
@@ -23,8 +26,10 @@ One GPU only: --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,6 +97,53 @@ def time_loop(fn, steps, warmup, stream):
     return start.elapsed_time(stop) / steps
 
 
+def time_graph(fn, reps, replays, stream):
+    """Mean ms per call of `fn` with `reps` calls captured in one HIP graph
+    (for kernels too short for per-call launches to keep the GPU busy)."""
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(reps):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        stop.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(stop) / (reps * replays)
+
+
+# Kernel sources behind the split-KV partial kernel; the committed counter
+# summary records their hash.
+PARTIAL_SOURCES = ("attn_stream.hpp", "common.hpp", "gqa_api.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_partial_hbm_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per partial launch from the committed FETCH_SIZE/WRITE_SIZE
+    summary (copy-calibrated), or None once the kernel sources differ from
+    the ones the counters were taken on."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    nbytes = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    digest = re.search(r"^source_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not nbytes or not digest:
+        return None
+    h = hashlib.sha256()
+    for name in PARTIAL_SOURCES:
+        with open(os.path.join(ROOT, "gqa_attention_forward_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return int(nbytes.group(1)) if h.hexdigest() == digest.group(1) else None
+
+
 def roof(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -150,11 +202,13 @@ def bench_decode(args, device, stream):
     gbs = total_bytes / (ms * 1e-3) / 1e9
     # dominant kernel alone: the split-KV partial kernel (reads Q, K, V once)
     ms_p = time_loop(partial, args.steps, max(1, args.warmup // 2), stream)
-    ms_m = time_loop(merge, args.steps, 1, stream)
+    # the merge kernel runs a few microseconds: time it from a captured graph
+    ms_m = time_graph(merge, 20, 5, stream)
     assert torch.isfinite(out.float()).all()
     return c, inp, {
         "ms_per_step": ms, "value": gbs, "total_bytes": total_bytes,
-        "roofline": roof("hbm", read_bytes / (ms_p * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "roofline": roof("hbm", read_bytes / (ms_p * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                         measured_traffic()),
         "kernel_ms": {"partial": round(ms_p, 5), "merge": round(ms_m, 5)},
         "kernel_bytes_per_launch": {"partial": read_bytes},
     }

@@ -143,36 +143,39 @@ attn_prefill_kernel(const AttnArgs a) {
     for (int i = 0; i < D / 32; ++i) acc[nb][i] = f32x16{};
   }
 
-  // ---- K/V staging: chunk ci = tid + i NT of a 64 x DC tile.  Keys at or
-  // past kend are never read (loads go to row kend - 1, the keys are masked)
-  auto krow = [&](int key) -> const uint16_t* {
-    if constexpr (PAGED) {
-      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
-      return a.k + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.k_sh;
-    } else {
-      return a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)key * a.k_ss;
-    }
-  };
-  auto vrow = [&](int key) -> const uint16_t* {
-    if constexpr (PAGED) {
-      const int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 6)];
-      return a.v + (int64_t)pg * a.kv_sp + (int64_t)(key & 63) * a.kv_sr + (int64_t)g * a.v_sh;
-    } else {
-      return a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)key * a.v_ss;
-    }
-  };
-  const int klast = kend - 1;
+  // ---- K/V staging: chunk ci = tid + i NT of a 64 x DC tile.  A 64-key
+  // tile is one page of the paged layout; its rows load through a buffer
+  // resource whose size ends at the tile's last row before kv_len, so rows
+  // past kv_len read as zeros without touching memory (and are masked).
+  // Each thread's offsets are constants; tile start and page are scalar.
   struct Stage {
     u32x4 k[CPT];
     u32x4 v[CPT];
   };
+  const uint32_t kss2 = (uint32_t)(PAGED ? a.kv_sr : a.k_ss) * 2u;
+  const uint32_t vss2 = (uint32_t)(PAGED ? a.kv_sr : a.v_ss) * 2u;
+  const uint32_t koff0 = (uint32_t)(tid / DC) * kss2 + 16u * (tid % DC);
+  const uint32_t voff0 = (uint32_t)(tid / DC) * vss2 + 16u * (tid % DC);
+  static_assert(NT % DC == 0, "row step");
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)a.page_table;
   auto load_tile = [&](int j0, Stage& st) {
+    const uint16_t *kp, *vp;
+    if constexpr (PAGED) {
+      const int pg = ptab[(int64_t)b * a.max_pages + (j0 >> 6)];
+      kp = a.k + (int64_t)pg * a.kv_sp + (int64_t)g * a.k_sh;
+      vp = a.v + (int64_t)pg * a.kv_sp + (int64_t)g * a.v_sh;
+    } else {
+      kp = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)j0 * a.k_ss;
+      vp = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)j0 * a.v_ss;
+    }
+    const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
+    const BufRes kr = make_bufres(kp, (valid - 1u) * kss2 + (uint32_t)D * 2u);
+    const BufRes vr = make_bufres(vp, (valid - 1u) * vss2 + (uint32_t)D * 2u);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + i * NT;
-      const int key = min(j0 + ci / DC, klast);
-      st.k[i] = *reinterpret_cast<const u32x4*>(krow(key) + 8 * (ci % DC));
-      st.v[i] = *reinterpret_cast<const u32x4*>(vrow(key) + 8 * (ci % DC));
+      st.k[i] = buf_load16v(kr, koff0 + (uint32_t)(i * (NT / DC)) * kss2);
+      st.v[i] = buf_load16v(vr, voff0 + (uint32_t)(i * (NT / DC)) * vss2);
     }
   };
   auto store_tile = [&](int stage, const Stage& st) {

@@ -81,6 +81,9 @@ __device__ __forceinline__ BufRes make_bufres(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+__device__ __forceinline__ u32x4 buf_load16v(BufRes r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
 __device__ __forceinline__ uint4 buf_load16(BufRes r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);

@@ -123,11 +123,11 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
   return check_launch("attention kernel");
 }
 
-template <int D, int NW, int NB, bool PAGED, bool PARTIAL>
+template <int D, int NW, bool PAGED, bool PARTIAL>
 gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  using C = gqa::PrefillCfg<D, NW, NB>;
+  using C = gqa::PrefillCfg<D, NW>;
   args.spw = 1;
-  return launch_grid(&gqa::attn_prefill_kernel<D, NW, NB, PAGED, PARTIAL>, C::LDS_BYTES, C::NT,
+  return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL>, C::LDS_BYTES, C::NT,
                      args, rows, C::ROWS, stream);
 }
 
@@ -184,11 +184,9 @@ template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
   if (rows <= 32) return launch_stream<D, 2, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 64) return launch_prefill<D, 2, 1, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 128) return launch_prefill<D, 4, 1, PAGED, PARTIAL>(args, rows, stream);
-  // 8 waves x 32 rows; the 4 waves x 64 rows form (NB = 2, one wave per
-  // SIMD) measured slower on the causal workload
-  return launch_prefill<D, 8, 1, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 64) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 128) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
+  return launch_prefill<D, 8, PAGED, PARTIAL>(args, rows, stream);
 }
 
 template <bool PAGED, bool PARTIAL>

@@ -162,11 +162,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_prefill_kernel(const AttnArgs
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
-  // ---- K/V staging.  A 64-key tile is one page of the paged layout; chunk
-  // i of a thread is row tid / DC + i NT / DC, loaded through a buffer
-  // resource that starts at that row and ends at the tile's last row before
-  // kv_len, so rows past kv_len read as zeros without touching memory (and
-  // are masked), and every chunk uses the same per-thread offset.
+  // ---- K/V staging.  A 64-key tile is one page of the paged layout; it is
+  // loaded through one buffer resource per tensor that starts at the tile
+  // and ends at its last row before kv_len, so rows past kv_len read as
+  // zeros without touching memory (and are masked).  Chunk i of a thread is
+  // row tid / DC + i NT / DC at a per-thread constant offset.
   struct Stage {
     u32x4 k[CPT];
     u32x4 v[CPT];
@@ -174,28 +174,32 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_prefill_kernel(const AttnArgs
   const uint32_t kss2 = (uint32_t)(PAGED ? a.kv_sr : a.k_ss) * 2u;
   const uint32_t vss2 = (uint32_t)(PAGED ? a.kv_sr : a.v_ss) * 2u;
   const int srow = tid / DC, sch = tid % DC;
-  const uint32_t koff0 = (uint32_t)srow * kss2 + 16u * sch;
-  const uint32_t voff0 = (uint32_t)srow * vss2 + 16u * sch;
+  uint32_t koff[CPT], voff[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    koff[i] = (uint32_t)(srow + i * (NT / DC)) * kss2 + 16u * sch;
+    voff[i] = (uint32_t)(srow + i * (NT / DC)) * vss2 + 16u * sch;
+  }
+  const uint16_t* khead = a.k + (PAGED ? (int64_t)g * a.k_sh
+                                       : (int64_t)b * a.k_sb + (int64_t)g * a.k_sh);
+  const uint16_t* vhead = a.v + (PAGED ? (int64_t)g * a.v_sh
+                                       : (int64_t)b * a.v_sb + (int64_t)g * a.v_sh);
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)a.page_table;
   auto load_tile = [&](int j0, Stage& st) {
-    const uint16_t *kp, *vp;
-    if constexpr (PAGED) {
-      const int pg = ptab[(int64_t)b * a.max_pages + (j0 >> 6)];
-      kp = a.k + (int64_t)pg * a.kv_sp + (int64_t)g * a.k_sh;
-      vp = a.v + (int64_t)pg * a.kv_sp + (int64_t)g * a.v_sh;
-    } else {
-      kp = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)j0 * a.k_ss;
-      vp = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)j0 * a.v_ss;
-    }
-    const int valid = min(BK, n - j0);  // >= 1: tiles start below kend <= n
+    int64_t off;
+    if constexpr (PAGED)
+      off = (int64_t)ptab[(int64_t)b * a.max_pages + (j0 >> 6)] * a.kv_sp;
+    else
+      off = (int64_t)j0 * a.k_ss;
+    const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
+    const BufRes kr = make_bufres(khead + off, (valid - 1u) * kss2 + (uint32_t)D * 2u);
+    const BufRes vr = make_bufres(vhead + (PAGED ? off : (int64_t)j0 * a.v_ss),
+                                  (valid - 1u) * vss2 + (uint32_t)D * 2u);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int r0 = i * (NT / DC), vr0 = valid - r0;  // valid rows from r0 on
-      const uint32_t kb = vr0 > 0 ? (uint32_t)(vr0 - 1) * kss2 + (uint32_t)D * 2u : 0u;
-      const uint32_t vb = vr0 > 0 ? (uint32_t)(vr0 - 1) * vss2 + (uint32_t)D * 2u : 0u;
-      st.k[i] = buf_load16v(make_bufres(kp + (int64_t)r0 * (kss2 / 2), kb), koff0);
-      st.v[i] = buf_load16v(make_bufres(vp + (int64_t)r0 * (vss2 / 2), vb), voff0);
+      st.k[i] = buf_load16v(kr, koff[i]);
+      st.v[i] = buf_load16v(vr, voff[i]);
     }
   };
   // the rows of a thread's chunks differ by multiples of 8: one swizzle
@@ -338,8 +342,85 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_prefill_kernel(const AttnArgs
     }
   };
 
+  // Whole-phase operand fetches (EARLY): each phase's LDS operands are
+  // requested before the previous phase's MFMAs, so none of its MFMAs waits
+  // on LDS latency.  Needs 2 x 32 more VGPRs; only the 8-wave form has them.
+  constexpr bool EARLY = (NW == 8);
+  auto kfetch = [&](const uint16_t* Ks, int h, bf16x8 (&k)[NCK]) {
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) k[c] = kread(Ks, c, h);
+  };
+  auto vfetch = [&](const uint16_t* Vs, int h, bf16x8 (&v)[2 * NDB]) {
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) v[i] = vread(Vs, 2 * h + i / NDB, i % NDB);
+  };
+  auto qk_reg = [&](const bf16x8 (&k)[NCK], auto interleave) {
+    constexpr bool IL = decltype(interleave)::value;
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[c], qf[c], s, 0, 0, 0);
+      if constexpr (IL) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);  // LDS reads (next phase)
+        __builtin_amdgcn_sched_group_barrier(0x0002, 8, 0);  // VALU
+      }
+    }
+    return s;
+  };
+  // interleave: 1 = vector work and next-phase LDS reads between the MFMAs,
+  // 2 = the next tile's LDS writes between the MFMAs
+  auto pv_reg = [&](const bf16x8 (&v)[2 * NDB], const bf16x8 (&pb)[2], auto interleave) {
+    constexpr int IL = decltype(interleave)::value;
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {
+      acc[i % NDB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[i], pb[i / NDB], acc[i % NDB], 0, 0, 0);
+      if constexpr (IL == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);  // LDS reads (next phase)
+        __builtin_amdgcn_sched_group_barrier(0x0002, 8, 0);  // VALU
+      } else if constexpr (IL == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0200, 1, 0);  // LDS write
+      }
+    }
+  };
+
   using True = std::integral_constant<bool, true>;
   using False = std::integral_constant<bool, false>;
+  auto step_early = [&](auto mask_tag, int it) {
+    const int j0 = kbeg + it * BK;
+    load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
+    const uint16_t* Ks = smem + (it & 1) * C::STAGE;
+    const uint16_t* Vs = Ks + C::KTILE;
+    bf16x8 k0[NCK], k1[NCK], v0[2 * NDB], v1[2 * NDB], p0[2], p1[2];
+    kfetch(Ks, 0, k0);
+    kfetch(Ks, 1, k1);
+    __builtin_amdgcn_sched_barrier(0);
+    // 1. S_0
+    f32x16 s0 = qk_reg(k0, False{});
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. S_1 || softmax of S_0; V_0 operands requested
+    vfetch(Vs, 0, v0);
+    f32x16 s1 = qk_reg(k1, True{});
+    const float alpha0 = softmax(mask_tag, j0, 0, s0, p0);
+    pin(p0);
+    __builtin_amdgcn_sched_barrier(0);
+    rescale(alpha0);
+    // 3. O += V_0 P_0 || softmax of S_1; V_1 operands requested
+    vfetch(Vs, 1, v1);
+    pv_reg(v0, p0, std::integral_constant<int, 1>{});
+    const float alpha1 = softmax(mask_tag, j0, 1, s1, p1);
+    pin(p1);
+    __builtin_amdgcn_sched_barrier(0);
+    rescale(alpha1);
+    // 4. stage the next tile into the idle buffer (no wave reads it before
+    // the barrier below), then O += V_1 P_1: the LDS writes overlap the MFMAs
+    store_tile((it + 1) & 1, nx);
+    pv_reg(v1, p1, std::integral_constant<int, 2>{});
+    lds_barrier();
+  };
   auto step = [&](auto mask_tag, int it) {
     const int j0 = kbeg + it * BK;
     // Unconditional prefetch of the next tile (past the end it re-reads the
@@ -370,8 +451,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_prefill_kernel(const AttnArgs
   };
 
   int it = 0;
-  for (; it < nfull; ++it) step(False{}, it);
-  for (; it < ntiles; ++it) step(True{}, it);
+  if constexpr (EARLY) {
+    for (; it < nfull; ++it) step_early(False{}, it);
+    for (; it < ntiles; ++it) step_early(True{}, it);
+  } else {
+    for (; it < nfull; ++it) step(False{}, it);
+    for (; it < ntiles; ++it) step(True{}, it);
+  }
 
   // ---- epilogue; accumulator register j of d-block db holds
   //      d = 32 db + 8 (j >> 2) + 4 hl + (j & 3) of query row `col`

@@ -179,6 +179,12 @@ SWEEP = [
     (1, 32, 4, 16, 700, 128),
     (3, 4, 4, 5, 129, 128),
     (2, 12, 3, 70, 70, 64),
+    # 33..64 and 65..128 query rows per (b, kv head): the 2- and 4-wave
+    # shared-tile forms, both head dims
+    (2, 8, 2, 12, 333, 128),
+    (2, 8, 2, 12, 333, 64),
+    (1, 16, 2, 12, 400, 128),
+    (1, 16, 2, 12, 400, 64),
 ]
 
 

@@ -70,12 +70,17 @@ def dense_flops(c):
     return 4 * c.d * pairs
 
 
-def paged_work(w):
+def paged_work(w, causal=False):
+    """Algorithmic bytes (Q, O, K, V once) and flops (4 d per visible pair)."""
     ql = w["q_len"].numpy().astype(np.int64)
     kl = w["kv_len"].numpy().astype(np.int64)
     Hq, Hkv, d = w["Hq"], w["Hkv"], w["d"]
     bytes_ = int((2 * ql * Hq * d * 2).sum() + (2 * kl * Hkv * d * 2).sum())
-    flops = int((4 * d * Hq * ql * kl).sum())
+    if causal:  # bottom-right: row i sees kv_len - q_len + i + 1 keys
+        pairs = ql * (kl - ql) + ql * (ql + 1) // 2
+    else:
+        pairs = ql * kl
+    flops = int((4 * d * Hq * pairs).sum())
     return bytes_, flops
 
 
@@ -268,6 +273,28 @@ def bench_secondary(args, device, stream):
         ms = time_loop(pstep, steps, warm_steps(pstep, stream), stream)
         res[f"ragged_paged_tile{tile}"] = {"ms": round(ms, 5), "bytes": pb, "flops": pf,
                                            "roofline_frac": round(t_roof / (ms * 1e-3), 4)}
+    # causal chunked prefill over a cached prefix (paged, bottom-right causal)
+    w = workloads.make_paged_chunked()
+    gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
+    outc = torch.empty_like(gw["q"])
+    cb, cf = paged_work(w, causal=True)
+    t_roof = max(cb / (HBM_PEAK_GBS * 1e9), cf / (BF16_PEAK_TFLOPS * 1e12))
+    for tile in (0, 1024):
+        ws = None
+        if tile:
+            ws = torch.empty(m.workspace_size(1, w["Hq"], w["total_q"],
+                                              gw["page_table"].shape[1] * 64, w["d"], tile),
+                             dtype=torch.uint8, device=device)
+
+        def cstep(tile=tile, ws=ws):
+            m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"], gw["page_table"],
+                    gw["kv_len"], max_q_len=w["max_q_len"], scale=w["scale"], sink=gw["sink"],
+                    causal=True, tile_s_kv=tile, out=outc, workspace=ws)
+        ms = time_loop(cstep, steps, warm_steps(cstep, stream), stream)
+        res[f"paged_causal_chunked_tile{tile}"] = {
+            "ms": round(ms, 5), "bytes": cb, "flops": cf,
+            "tflops": round(cf / (ms * 1e-3) / 1e12, 2),
+            "roofline_frac": round(t_roof / (ms * 1e-3), 4)}
     # tiny prefill (launch-bound)
     c, _, g = setup_dense("tiny_prefill", device)
     step, out = prefill_step_fn(g, c, 0)
@@ -298,6 +325,16 @@ def run_only(args, device, stream):
                              gw["page_table"], gw["kv_len"], max_q_len=w["max_q_len"],
                              scale=w["scale"], sink=gw["sink"], tile_s_kv=1024)
         return {"workload": name, "ms": time_loop(fn, args.steps, args.warmup, stream)}
+    if name == "paged_causal_chunked":
+        w = workloads.make_paged_chunked()
+        gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
+        m = gqa()
+        fn = lambda: m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],  # noqa: E731
+                             gw["page_table"], gw["kv_len"], max_q_len=w["max_q_len"],
+                             scale=w["scale"], sink=gw["sink"], causal=True)
+        ms = time_loop(fn, args.steps, args.warmup, stream)
+        return {"workload": name, "ms": ms,
+                "TFLOP/s": paged_work(w, causal=True)[1] / (ms * 1e-3) / 1e12}
     c, _, g = setup_dense(name, device)
     step, _ = prefill_step_fn(g, c, 2048 if name == "shortq_longkv" else 0)
     ms = time_loop(step, args.steps, args.warmup, stream)
@@ -343,7 +380,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--only", choices=["decode_partial", "shortq_longkv", "causal_prefill",
-                                       "ragged_paged", "copy"],
+                                       "ragged_paged", "paged_causal_chunked", "copy"],
                     help="profiling aid: time only this workload's kernels and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -152,6 +152,25 @@ def test_paged_causal_chunked_prefill(tile):
                  f"paged causal tile={tile}")
 
 
+@pytest.mark.parametrize("tile", [0, 1024])
+def test_paged_causal_chunked_full(tile):
+    """The timed chunked-prefill workload (8 chunks of 512 over prefixes up to
+    3584, Hq=32, Hkv=1, sink): sampled rows against the oracle row by row."""
+    note(f"paged causal chunked prefill, full size, tile={tile}")
+    w = workloads.make_paged_chunked()
+    out = _paged_run(w, causal=True, tile=tile)
+    r = np.random.default_rng(5 + tile)
+    cu = w["cu_seqlens_q"].numpy()
+    t = r.integers(0, w["total_q"], 96)
+    t[:2 * w["B"]] = np.concatenate([cu[:-1], cu[1:] - 1])  # first and last row of every chunk
+    h = r.integers(0, w["Hq"], t.size)
+    want = oracle.paged_attention_rows_fp64(w["q"].float().numpy(), cu, w["k_cache"].float().numpy(),
+                                            w["v_cache"].float().numpy(), w["page_table"].numpy(),
+                                            w["kv_len"].numpy(), t, h, scale=w["scale"],
+                                            page_size=64, sink=to_f64(w["sink"]), causal=True)
+    assert_close(out[t, h], want, f"paged causal chunked full tile={tile}")
+
+
 @pytest.mark.parametrize("G", [4, 32])
 @pytest.mark.parametrize("tile", [0, 1024])
 def test_paged_decode_shape(G, tile):

@@ -70,6 +70,7 @@ CASES = {
 }
 
 PAGED_SEED = 1005
+CHUNKED_SEED = 1006
 
 
 def make_dense(B, Hq, Hkv, Sq, Skv, d, seed, *, kv_len=None, sink=False,
@@ -162,6 +163,22 @@ def make_paged(B=8, Hq=32, Hkv=1, d=128, *, max_q=64, max_kv=4096, page_size=64,
         "max_q_len": int(q_lens.max()), "total_q": total_q, "B": B, "Hq": Hq, "Hkv": Hkv,
         "d": d,
     }
+
+
+def make_paged_chunked(B=8, Hq=32, Hkv=1, d=128, *, chunk=512, max_prefix=3584,
+                       seed=CHUNKED_SEED):
+    """Causal chunked prefill over a cached prefix, same heads as the paged workload.
+
+    Each sequence appends a chunk of `chunk` query tokens to a cached prefix of
+    prefix_b ~ U[0, max_prefix] tokens, so kv_len_b = prefix_b + chunk and the
+    chunk's row i sees keys 0 .. prefix_b + i (bottom-right aligned causal).
+    Draw order: the prefixes from `seed`, then everything else as in
+    `make_paged` from `seed + 1`.
+    """
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    prefix = torch.randint(0, max_prefix + 1, (B,), generator=g, dtype=torch.int64)
+    return make_paged(B, Hq, Hkv, d, max_q=chunk, max_kv=max_prefix + chunk, seed=seed + 1,
+                      q_lens=[chunk] * B, kv_lens=(prefix + chunk).tolist())
 
 
 def to_f64(t) -> np.ndarray:

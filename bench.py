@@ -166,7 +166,7 @@ def roof(bound, achieved, peak, unit, traffic=None):
 # ---------------------------------------------------------------- workloads
 
 def setup_dense(name, device):
-    c = workloads.CASES[name]
+    c = workloads.CASES[name] if name in workloads.CASES else workloads.HEAD_DIM_CASES[name]
     inp = workloads.make_case(c)
     g = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     return c, inp, g
@@ -252,6 +252,24 @@ def bench_secondary(args, device, stream):
         "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2), "flops": fl,
         "roofline": roof("mfma", fl / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s")}
     del g, out
+    # the other head dims: decode at d = 256, causal prefill at d = 32 and 256
+    c, _, g = setup_dense("decode_splitkv_d256", device)
+    step, _, _, _ = decode_step_fns(g, c)
+    ms = time_loop(step, steps, warm_steps(step, stream), stream)
+    tb, _ = dense_bytes(c)
+    res["decode_splitkv_d256"] = {
+        "ms": round(ms, 5), "GB/s": round(tb / (ms * 1e-3) / 1e9, 1),
+        "roofline": roof("hbm", tb / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    del g
+    for name in ("causal_prefill_d32", "causal_prefill_d256"):
+        c, _, g = setup_dense(name, device)
+        step, out = prefill_step_fn(g, c, 0)
+        ms = time_loop(step, steps, warm_steps(step, stream), stream)
+        fl = dense_flops(c)
+        res[name] = {
+            "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2), "flops": fl,
+            "roofline": roof("mfma", fl / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s")}
+        del g, out
     # ragged paged with sink: one pass and split-KV (tiles of 1024 keys)
     w = workloads.make_paged()
     gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}

@@ -3,7 +3,8 @@
 // kv split); all NW waves share each 64-key K/V tile through LDS, so a tile
 // is fetched once per workgroup for every query head of the group (AstrAI
 // commit log, the commit that packs HB = min(G, warps) query heads per
-// block).  Each wave owns 32 query rows; two waves per SIMD.
+// block).  Each wave owns 32 query rows; two waves per SIMD (one workgroup
+// per CU at d = 256, whose double-buffered tiles take 130 KiB of LDS).
 //
 // MFMA mapping, v_mfma_f32_32x32x16_bf16 (32 query rows are the N
 // dimension):
@@ -58,6 +59,8 @@ struct PrefillCfg {
   static constexpr int TILE = BK * D;        // elements of one V tile
   static constexpr int STAGE = KTILE + TILE; // K then V
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  // workgroups per CU that fit in 160 KiB of LDS (one at d = 256)
+  static constexpr int WG_PER_CU = 2 * LDS_BYTES <= 160 * 1024 ? 2 : 1;
   static constexpr int CPT = BK * DC / NT;   // chunks per thread per tensor
   static_assert(CPT >= 1 && BK * DC % NT == 0 && NT % DC == 0, "tile split");
   static_assert((NT / DC) % 8 == 0, "chunk rows keep the V swizzle");
@@ -78,7 +81,8 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 }
 
 template <int D, int NW, bool PAGED, bool PARTIAL>
-__global__ void __launch_bounds__(NW * 64, 2) attn_prefill_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(NW * 64, (PrefillCfg<D, NW>::WG_PER_CU))
+attn_prefill_kernel(const AttnArgs a) {
   using C = PrefillCfg<D, NW>;
   constexpr int NT = C::NT;
   constexpr int BK = C::BK;
@@ -344,8 +348,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_prefill_kernel(const AttnArgs
 
   // Whole-phase operand fetches (EARLY): each phase's LDS operands are
   // requested before the previous phase's MFMAs, so none of its MFMAs waits
-  // on LDS latency.  Needs 2 x 32 more VGPRs; only the 8-wave form has them.
-  constexpr bool EARLY = (NW == 8);
+  // on LDS latency.  Needs 2 x D / 4 more VGPRs; only the 8-wave form at
+  // d <= 128 has them.
+  constexpr bool EARLY = (NW == 8 && D <= 128);
   auto kfetch = [&](const uint16_t* Ks, int h, bf16x8 (&k)[NCK]) {
 #pragma unroll
     for (int c = 0; c < NCK; ++c) k[c] = kread(Ks, c, h);

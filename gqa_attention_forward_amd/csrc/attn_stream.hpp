@@ -44,12 +44,25 @@ struct StreamCfg {
   static constexpr int SLOT_F = NQB * (2 + 4 * NDB) * 64;  // combine floats per wave
   static constexpr int PSTR = D + 4;       // parked column: O (D floats), m, l, pad
   static constexpr int PEND_F = NQB * 16 * PSTR;  // parked floats per split
-  static constexpr int MAX_SPW = NQB == 1 ? 8 : 4;  // splits per workgroup (LDS bound)
-  // LDS: one V tile per wave, one combine slot per wave other than 0, and
-  // (partial mode) one parked state per split of the run
+  // d = 256 keeps Q in LDS (row pitch D + 8: conflict-free operand reads)
+  static constexpr bool Q_LDS = D > 128;
+  static constexpr int QP = D + 8;
+  static constexpr int QTILE = Q_LDS ? NQB * 16 * QP : 0;
+  // LDS: one V tile per wave, one combine slot per wave other than 0,
+  // (partial mode) one parked state per split of the run, and Q at d = 256
   static constexpr int lds_bytes(int nw, int spw) {
-    return nw * VTILE * 2 + (nw - 1) * SLOT_F * 4 + spw * PEND_F * 4;
+    return nw * VTILE * 2 + (nw - 1) * SLOT_F * 4 + spw * PEND_F * 4 + QTILE * 2;
   }
+  static constexpr int LDS_LIMIT = 160 * 1024;
+  // splits per workgroup: up to 8 (one 16-column block) or 4, as LDS allows
+  static constexpr int max_spw(int nw) {
+    int s = NQB == 1 ? 8 : 4;
+    while (s > 1 && lds_bytes(nw, s) > LDS_LIMIT) s /= 2;
+    return s;
+  }
+  // the wider (4-wave) form needs its combine slots and one parked split
+  static constexpr bool FOUR_WAVES = lds_bytes(4, 1) <= LDS_LIMIT;
+  static_assert(lds_bytes(2, max_spw(2)) <= LDS_LIMIT, "two-wave form fits in LDS");
 };
 
 // One wave per SIMD: the register budget then holds two in-flight tiles,
@@ -63,6 +76,12 @@ attn_stream_kernel(const AttnArgs a) {
   // tiles in flight per wave while it computes on one (a deeper rotation
   // measured no faster and needs one wave per SIMD)
   constexpr int DEPTH = 1;
+  // At d = 256 a tile is 128 VGPRs, and Q and two whole tiles would not fit
+  // the 256 arch VGPRs: the next tile's V loads are issued once the current
+  // V is in LDS and its K loads once the current K has been through the
+  // MFMAs, so one tile's worth of K/V is live.  That still keeps as many
+  // bytes in flight per wave as a whole d = 128 tile.
+  constexpr bool LATE = D > 128;
   constexpr int BK = C::BK;
   constexpr int NC = C::NC;
   constexpr int NDB = C::NDB;
@@ -140,6 +159,27 @@ attn_stream_kernel(const AttnArgs a) {
                              : bf16x8{};
   }
 
+  // d = 256: Q goes to LDS once (wave 0 writes, every wave reads it per tile)
+  uint16_t* qlds = smem + NW * C::VTILE + 2 * ((NW - 1) * C::SLOT_F) +
+                   2 * (PARTIAL ? a.spw * C::PEND_F : 0);
+  if constexpr (C::Q_LDS) {
+    if (wv == 0) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          *reinterpret_cast<bf16x8*>(qlds + (qb * 16 + c16) * C::QP + 32 * c + 8 * grp) =
+              qf[qb][c];
+    }
+    lds_barrier();
+  }
+  auto qop = [&](int qb, int c) {
+    if constexpr (C::Q_LDS)
+      return *reinterpret_cast<const bf16x8*>(qlds + (qb * 16 + c16) * C::QP + 32 * c + 8 * grp);
+    else
+      return qf[qb][c];
+  };
+
   float m[NQB], l[NQB];
   f32x4 acc[NQB][NDB];
 #pragma unroll
@@ -197,22 +237,73 @@ attn_stream_kernel(const AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16(vr, voff + (uint32_t)j * vstep);
   };
+  // the K (which = 0) or V (which = 1) half of `load`, for the late-issue order
+  auto tile_res = [&](int j0, int which) {
+    const uint16_t* p;
+    if constexpr (PAGED) {
+      const int pg = ptab[(int64_t)b * a.max_pages + (j0 >> 6)];
+      const int64_t off = (int64_t)pg * a.kv_sp + (int64_t)(j0 & 63) * a.kv_sr;
+      p = which ? a.v + off + (int64_t)g * a.v_sh : a.k + off + (int64_t)g * a.k_sh;
+    } else {
+      p = which ? a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)j0 * a.v_ss
+                : a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)j0 * a.k_ss;
+    }
+    const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
+    return make_bufres(p, (valid - 1u) * (which ? vss2 : kss2) + (uint32_t)D * 2u);
+  };
+  auto load_k = [&](int j0, Tile& t) {
+    const BufRes kr = tile_res(j0, 0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16(kr, koff[kb] + 64u * c);
+  };
+  auto load_v = [&](int j0, Tile& t) {
+    const BufRes vr = tile_res(j0, 1);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16(vr, voff, (uint32_t)j * vstep);
+  };
 
   uint16_t* vbuf = smem + wv * C::VTILE;
   float* slots = reinterpret_cast<float*>(smem + NW * C::VTILE);
   float* pend = slots + (NW - 1) * C::SLOT_F;  // parked split states (partial mode)
 
-  auto compute = [&](int j0, const Tile& t) {
-    // V tile -> wave-private LDS (row-major, swizzled 16-byte slots)
+  // At d = 256 the swizzle repeats every 8 key rows: V row writes need 4
+  // per-lane LDS offsets and the transposing reads 8 (one per d block mod 8),
+  // with the rest as immediates.  (Recomputing all 16 + 32 offsets per lane
+  // costs more registers than the tiles leave.)
+  constexpr int RPJ = 64 / DC;                    // V rows per 64-lane chunk step
+  constexpr int WPER = RPJ >= 8 ? 1 : 8 / RPJ;    // chunk steps per swizzle period
+  constexpr int RPER = NDB < 8 ? NDB : 8;
+  int vwo[WPER], vro[RPER];
+  if constexpr (LATE) {
+#pragma unroll
+    for (int jl = 0; jl < WPER; ++jl) {
+      const int kl = lane / DC + RPJ * jl;
+      vwo[jl] = kl * D + 8 * ((lane % DC) ^ vslot_swz<DC>(kl));
+    }
+    const int kl0 = 4 * grp + (c16 >> 2);
+    const int sw = vslot_swz<DC>(kl0);
+#pragma unroll
+    for (int dl = 0; dl < RPER; ++dl)
+      vro[dl] = kl0 * D + 8 * ((2 * dl + ((c16 & 3) >> 1)) ^ sw) + 4 * (c16 & 1);
+  }
+  // V tile -> wave-private LDS (row-major, swizzled 16-byte slots)
+  auto stage_v = [&](const Tile& t) {
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      const int ci = lane + 64 * j;
-      const int kl = ci / DC;
-      const int slot = (ci % DC) ^ vslot_swz<DC>(kl);
-      *reinterpret_cast<uint4*>(vbuf + kl * D + 8 * slot) = t.v[j];
+      if constexpr (LATE) {
+        *reinterpret_cast<uint4*>(vbuf + vwo[j % WPER] + (j / WPER) * 8 * D) = t.v[j];
+      } else {
+        const int ci = lane + 64 * j;
+        const int kl = ci / DC;
+        const int slot = (ci % DC) ^ vslot_swz<DC>(kl);
+        *reinterpret_cast<uint4*>(vbuf + kl * D + 8 * slot) = t.v[j];
+      }
     }
-    // S^T = K Q^T for two 16-key blocks
-    f32x4 s[NQB][2];
+  };
+  // S^T = K Q^T for two 16-key blocks
+  auto qk = [&](const Tile& t, f32x4 (&s)[NQB][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -221,8 +312,11 @@ attn_stream_kernel(const AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, t.k[kb][c]), qf[qb][c], s[qb][kb], 0, 0, 0);
+              __builtin_bit_cast(bf16x8, t.k[kb][c]), qop(qb, c), s[qb][kb], 0, 0, 0);
       }
+  };
+  // mask, online softmax and O^T += V^T P^T of the tile at key j0
+  auto finish = [&](int j0, f32x4 (&s)[NQB][2]) {
     // register r of block kb holds key j0 + 16 kb + 4 grp + r
     if (j0 + BK > wlo) {
 #pragma unroll
@@ -263,10 +357,17 @@ attn_stream_kernel(const AttnArgs a) {
       i16x4 va[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int kl = 16 * half + 4 * grp + (c16 >> 2);
-        const int slot = (2 * db + ((c16 & 3) >> 1)) ^ vslot_swz<DC>(kl);
+        const uint16_t* src;
+        if constexpr (LATE) {
+          // slot (2 db + x) ^ sw = 16 (db / 8) + ((2 (db % 8) + x) ^ sw), sw < 16
+          src = vbuf + vro[db % RPER] + 16 * half * D + 128 * (db / RPER);
+        } else {
+          const int kl = 16 * half + 4 * grp + (c16 >> 2);
+          const int slot = (2 * db + ((c16 & 3) >> 1)) ^ vslot_swz<DC>(kl);
+          src = vbuf + kl * D + 8 * slot + 4 * (c16 & 1);
+        }
         va[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vbuf + kl * D + 8 * slot + 4 * (c16 & 1)));
+            (__attribute__((address_space(3))) i16x4*)(src));
       }
       const bf16x8 vv = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(va[0], va[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -274,6 +375,11 @@ attn_stream_kernel(const AttnArgs a) {
       for (int qb = 0; qb < NQB; ++qb)
         acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb[qb], acc[qb][db], 0, 0, 0);
     }
+  };
+  auto compute = [&](int j0, const Tile& t) {
+    f32x4 s[NQB][2];
+    qk(t, s);
+    finish(j0, s);
   };
 
   // ---- end of a split: combine the NW waves' states through LDS (wave 0
@@ -403,10 +509,25 @@ attn_stream_kernel(const AttnArgs a) {
         for (int u = 0; u <= DEPTH; ++u) {
           if (k + u >= mine) goto keys_done;
           enter(k + u);
-          load(tile_key(k + u + DEPTH), t[(u + DEPTH) % (DEPTH + 1)]);
-          // keep the prefetch ahead of the first wait on tile k + u
-          __builtin_amdgcn_sched_barrier(0);
-          compute(tile_key(k + u), t[u]);
+          Tile& nx = t[(u + DEPTH) % (DEPTH + 1)];
+          if constexpr (!LATE) {
+            load(tile_key(k + u + DEPTH), nx);
+            // keep the prefetch ahead of the first wait on tile k + u
+            __builtin_amdgcn_sched_barrier(0);
+            stage_v(t[u]);
+            compute(tile_key(k + u), t[u]);
+          } else {
+            // next V once this V is in LDS, next K once this K has been used
+            stage_v(t[u]);
+            load_v(tile_key(k + u + DEPTH), nx);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 s[NQB][2];
+            qk(t[u], s);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(tile_key(k + u + DEPTH), nx);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(tile_key(k + u), s);
+          }
         }
       }
     }
@@ -418,14 +539,16 @@ attn_stream_kernel(const AttnArgs a) {
   }
 
   // ---- split partials: the run's parked states go out with coalesced
-  // stores, two query columns per wave instruction.  Global stores stay out
+  // stores, two query columns per wave instruction (one at d = 256).  Global stores stay out
   // of the key loop, where the registers they read would have to be guarded
   // by waits that also hold back the prefetch.
   if constexpr (PARTIAL) {
     lds_barrier();
-    constexpr int LPC = D / 4;  // lanes per column (float4 each)
-    const int half = lane >> 5, ln = lane & 31;
-    for (int it = 2 * wv + half; it < nsp * NQB * 16; it += 2 * NW) {
+    constexpr int LPC = D / 4;              // lanes per column (float4 each)
+    constexpr int CPI = LPC <= 32 ? 2 : 1;  // columns per wave instruction
+    const int half = CPI == 2 ? lane >> 5 : 0;
+    const int ln = CPI == 2 ? lane & 31 : lane;
+    for (int it = CPI * wv + half; it < nsp * NQB * 16; it += CPI * NW) {
       const int s = it / (NQB * 16);
       const int qb = (it / 16) % NQB;
       const int col = it % 16;

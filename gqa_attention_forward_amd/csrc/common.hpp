@@ -88,6 +88,11 @@ __device__ __forceinline__ uint4 buf_load16(BufRes r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// per-lane offset `off` plus a wave-uniform offset `soff` (held in an SGPR)
+__device__ __forceinline__ uint4 buf_load16(BufRes r, uint32_t off, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -110,13 +115,20 @@ __device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 3
 // half-wave from 64 four-byte banks, so the four (prefill) or eight (stream)
 // key rows one half-wave gathers from must land on disjoint slot groups;
 // this swizzle makes both gather shapes, and the b128 row writes,
-// bank-conflict free.
+// bank-conflict free.  Rows of 256 bytes or more (DC >= 16) all start on bank
+// 0, so keys 0-7 take eight different 32-byte slot pairs; a 128-byte row
+// shares the bank window with its neighbour (key bit 0 picks the half), and
+// four 64-byte rows fill a window by themselves.  The value always has bit 0
+// clear, which keeps each 32-byte pair together, and stays below DC.
 template <int DC>
 __device__ __forceinline__ int vslot_swz(int key) {
-  if constexpr (DC == 16)
+  static_assert(DC == 4 || DC == 8 || DC == 16 || DC == 32, "head dim 32, 64, 128 or 256");
+  if constexpr (DC >= 16)
     return ((key & 3) << 2) | (((key >> 2) & 1) << 1);
-  else
+  else if constexpr (DC == 8)
     return (((key >> 1) & 1) << 2) | (((key >> 2) & 1) << 1);
+  else
+    return ((key >> 2) & 1) << 1;
 }
 
 // Workgroup barrier that orders LDS only: global loads in flight (prefetch)

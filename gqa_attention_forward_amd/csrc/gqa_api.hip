@@ -63,11 +63,13 @@ gqa_status_t check_scale(float scale) {
   return GQA_OK;
 }
 
+bool head_dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
 gqa_status_t check_heads(int32_t Hq, int32_t Hkv, int32_t d) {
   if (Hq < 1 || Hkv < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "Hq and Hkv must be >= 1");
   if (Hq % Hkv != 0)
     return fail(GQA_ERR_INVALID_ARGUMENT, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
-  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 32, 64, 128, 256)", d);
   return GQA_OK;
 }
 
@@ -152,7 +154,7 @@ gqa_status_t launch_stream_nw(gqa::AttnArgs args, int64_t rows, hipStream_t stre
   using C = gqa::StreamCfg<D, NQB>;
   return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL>,
                      C::lds_bytes(NW, PARTIAL ? args.spw : 0), NW * 64, args, rows, 16 * NQB,
-                     stream, C::lds_bytes(NW, PARTIAL ? C::MAX_SPW : 0));
+                     stream, C::lds_bytes(NW, PARTIAL ? C::max_spw(NW) : 0));
 }
 
 // Launch shape of the stream kernel.  Split-KV runs: each workgroup takes
@@ -161,38 +163,61 @@ gqa_status_t launch_stream_nw(gqa::AttnArgs args, int64_t rows, hipStream_t stre
 // the 16 x 8-head x 8-split decode: 1 split per workgroup 98-99 us, 2 or 4
 // splits 95-96 us).  Two waves per workgroup once there are at least as
 // many workgroups as CUs (the same decode: 2 waves per workgroup beat 4);
-// four when the grid is smaller, to use more of each CU.
+// four when the grid is smaller, to use more of each CU (where the four
+// waves' combine slots fit in LDS: not for 32-row groups at d = 256).
 template <int D, int NQB, bool PAGED, bool PARTIAL>
 gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+  using C = gqa::StreamCfg<D, NQB>;
   const int64_t cus = device_cus();
   const int64_t per_split = (int64_t)args.B * args.Hkv * cdiv(rows, 16 * NQB);
   int spw = 1;
   if (PARTIAL)
-    while (spw * 2 <= gqa::StreamCfg<D, NQB>::MAX_SPW && spw * 2 <= args.n_split &&
+    while (spw * 2 <= C::max_spw(2) && spw * 2 <= args.n_split &&
            per_split * cdiv(args.n_split, spw * 2) >= cus)
       spw *= 2;
   args.spw = spw;
   const int64_t nblocks = per_split * cdiv(args.n_split, spw);
-  if (nblocks < cus) return launch_stream_nw<D, NQB, 4, PAGED, PARTIAL>(args, rows, stream);
+  if constexpr (C::FOUR_WAVES)
+    if (nblocks < cus) return launch_stream_nw<D, NQB, 4, PAGED, PARTIAL>(args, rows, stream);
   return launch_stream_nw<D, NQB, 2, PAGED, PARTIAL>(args, rows, stream);
 }
 
 // Kernel choice by query rows per (b, kv head): groups of up to 32 rows
 // (decode, short query blocks) stream keys per wave; larger groups share
 // K/V tiles across the waves of a workgroup, 32 rows per wave.
+// The prefill kernel's widths per head dim: a 64-key tile splits into whole
+// 16-byte chunks per thread from 2 waves up at d = 32 only up to 4 waves; the
+// V swizzle needs 4 or more waves at d = 256, where one workgroup per CU
+// with 4 waves (one per SIMD) holds the 32-row O and Q of a wave in
+// registers without spilling.
 template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 32) return launch_stream<D, 2, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 64) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
-  if (rows <= 128) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
-  return launch_prefill<D, 8, PAGED, PARTIAL>(args, rows, stream);
+  if (rows <= 32) {
+    // two 16-column blocks of Q do not fit beside the d = 256 tiles: two q-tiles
+    if constexpr (D == 256)
+      return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
+    else
+      return launch_stream<D, 2, PAGED, PARTIAL>(args, rows, stream);
+  }
+  if constexpr (D == 256) {
+    return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
+  } else {
+    if (rows <= 64) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
+    if (D == 32 || rows <= 128) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
+    if constexpr (D != 32) return launch_prefill<D, 8, PAGED, PARTIAL>(args, rows, stream);
+  }
+  return GQA_OK;  // not reached
 }
 
 template <bool PAGED, bool PARTIAL>
 gqa_status_t dispatch(gqa::AttnArgs args, int d, int64_t rows, hipStream_t stream) {
-  if (d == 64) return dispatch_rows<64, PAGED, PARTIAL>(args, rows, stream);
-  return dispatch_rows<128, PAGED, PARTIAL>(args, rows, stream);
+  switch (d) {
+    case 32: return dispatch_rows<32, PAGED, PARTIAL>(args, rows, stream);
+    case 64: return dispatch_rows<64, PAGED, PARTIAL>(args, rows, stream);
+    case 128: return dispatch_rows<128, PAGED, PARTIAL>(args, rows, stream);
+    default: return dispatch_rows<256, PAGED, PARTIAL>(args, rows, stream);
+  }
 }
 
 gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int32_t B,
@@ -206,14 +231,13 @@ gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int
   const int64_t nblocks = cdiv(rows, 4);
   if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   (void)hipGetLastError();
-  if (d == 64)
-    hipLaunchKernelGGL(gqa::merge_kernel<64>, dim3((unsigned)nblocks), dim3(256), 0, stream, ml, ot,
-                       reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq, n_split,
-                       rows);
-  else
-    hipLaunchKernelGGL(gqa::merge_kernel<128>, dim3((unsigned)nblocks), dim3(256), 0, stream, ml,
-                       ot, reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq,
-                       n_split, rows);
+  auto kern = d == 32 ? gqa::merge_kernel<32>
+              : d == 64 ? gqa::merge_kernel<64>
+              : d == 128 ? gqa::merge_kernel<128>
+                         : gqa::merge_kernel<256>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(256), 0, stream, ml, ot,
+                     reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq, n_split,
+                     rows);
   return check_launch("merge kernel");
 }
 
@@ -391,7 +415,7 @@ gqa_status_t gqa_attention_splitkv_merge(const void* workspace, size_t workspace
                                          const float* sink, void* stream) {
   if (B < 0 || Sq < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "B and Sq must be >= 0");
   if (Hq < 1 || n_split < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "Hq and n_split must be >= 1");
-  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 32, 64, 128, 256)", d);
   const int64_t rows = (int64_t)B * Hq * Sq;
   if (rows == 0) return ok();
   GQA_TRY(check_ptr("o", o));

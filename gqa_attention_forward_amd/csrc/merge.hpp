@@ -7,17 +7,18 @@ namespace gqa {
 
 // Split-KV merge (kernbench2 benches commit log: the (m, l, O) state and its
 // associative merge; nvfp4-megamoe-kernel commit log: normalise once).
-// One 64-lane wave per query row; D / 64 output elements per lane.
+// One 64-lane wave per query row; D / 64 output elements per lane (one per
+// lane of the first 32 at d = 32).
 template <int D>
 __global__ void __launch_bounds__(256)
 merge_kernel(const float2* __restrict__ ml, const float* __restrict__ ot, uint16_t* o,
              int64_t o_sb, int64_t o_sh, int64_t o_ss, const float* sink, int Hq, int Sq,
              int n_split, int64_t rows) {
-  constexpr int E = D / 64;
+  constexpr int E = D >= 64 ? D / 64 : 1;
   constexpr int CH = 8;  // partial states loaded per round
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  if (row >= rows || lane * E >= D) return;
   const int i = (int)(row % Sq);
   const int h = (int)((row / Sq) % Hq);
   const int64_t b = row / ((int64_t)Sq * Hq);
@@ -66,7 +67,10 @@ merge_kernel(const float2* __restrict__ ml, const float* __restrict__ ot, uint16
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = (M == -INFINITY) ? 0.f : accv[e] * inv;
   uint16_t* op = o + b * o_sb + (int64_t)h * o_sh + (int64_t)i * o_ss + lane * E;
-  if constexpr (E == 2) {
+  if constexpr (E == 4) {
+    *reinterpret_cast<uint2*>(op) =
+        make_uint2(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]));
+  } else if constexpr (E == 2) {
     *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(out[0], out[1]);
   } else {
     *reinterpret_cast<__bf16*>(op) = (__bf16)out[0];

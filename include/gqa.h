@@ -50,7 +50,9 @@
  *    bf16 tensors multiples of 8 elements, else GQA_ERR_UNSUPPORTED.  The
  *    stride between consecutive key rows of K and V (dense s stride, paged
  *    kv_stride_row) must be below 2^26 elements, else GQA_ERR_UNSUPPORTED.
- *    d must be 64 or 128, else GQA_ERR_UNSUPPORTED.
+ *    d must be 32, 64, 128 or 256, else GQA_ERR_UNSUPPORTED (the AstrAI
+ *    commit log's kernels cover prefill at head dim 32 and decode at 256
+ *    besides 64 and 128).
  *
  * Ownership: the caller owns all memory and keeps it alive until the work
  * enqueued on `stream` completes.  The library never allocates, frees,

@@ -89,7 +89,8 @@ int main(void) {
   expect("paged NULL cu", PAGED(NULL, P, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("paged NULL table", PAGED(P, NULL, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("paged NULL kv_len", PAGED(P, P, NULL, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
-  expect("paged d 256", PAGED(P, P, P, 64, 256, 0), GQA_ERR_UNSUPPORTED);
+  expect("paged d 512", PAGED(P, P, P, 64, 512, 0), GQA_ERR_UNSUPPORTED);
+  expect("paged d 48", PAGED(P, P, P, 64, 48, 0), GQA_ERR_UNSUPPORTED);
   expect("paged causal 3", PAGED(P, P, P, 64, 128, 3), GQA_ERR_INVALID_ARGUMENT);
   expect("paged split, no workspace",
          gqa_attention_paged(P, 4096, 128, P, P, P, 8192, 128, 128, P, 64, P, P, 4096, 128, 8, 32,

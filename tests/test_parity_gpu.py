@@ -95,9 +95,11 @@ def _rows(c, n, seed):
     return b, h, i
 
 
-@pytest.mark.parametrize("name", ["decode_splitkv", "shortq_longkv", "causal_prefill"])
+@pytest.mark.parametrize("name", ["decode_splitkv", "shortq_longkv", "causal_prefill",
+                                  "decode_splitkv_d256", "causal_prefill_d32",
+                                  "causal_prefill_d256"])
 def test_full_size_sampled(name):
-    c = workloads.CASES[name]
+    c = workloads.CASES.get(name) or workloads.HEAD_DIM_CASES[name]
     note(f"{name} full size {c}")
     inp = workloads.make_case(c)
     tile = c.tile_s_kv if c.decode else (2048 if name == "shortq_longkv" else 0)
@@ -218,6 +220,55 @@ def test_sweep(shape, causal, tile):
     got = run_dense(inp, causal=causal, tile=tile)
     want = oracle_dense(inp, causal=causal)
     assert_close(got, want, f"{shape} c={causal} t={tile}")
+
+
+# head dims 32 and 256 (AstrAI commit log: scalar prefill at d = 32, scalar
+# decode at d = 256), through every kernel form: one 16-column block (rows
+# <= 16), two (rows <= 32; two q-tiles at d = 256), and the shared-tile
+# prefill kernel at 2 and 4 waves (d = 32) or 4 waves (d = 256)
+SWEEP_HD = [
+    # B, Hq, Hkv, Sq, Skv
+    (2, 8, 2, 1, 500),
+    (2, 8, 2, 6, 333),
+    (2, 8, 2, 12, 333),
+    (1, 16, 2, 12, 400),
+    (2, 8, 2, 37, 301),
+]
+
+
+@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("shape", SWEEP_HD)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tile", [0, 64, 192])
+def test_sweep_head_dims(d, shape, causal, tile):
+    B, Hq, Hkv, Sq, Skv = shape
+    note(f"head dim sweep d={d} {shape} causal={causal} tile={tile}")
+    inp = workloads.make_dense(B, Hq, Hkv, Sq, Skv, d, seed=hash((shape, causal, d)) % 10000,
+                               kv_len="random", sink=True, nan_pad=True)
+    got = run_dense(inp, causal=causal, tile=tile)
+    want = oracle_dense(inp, causal=causal)
+    assert_close(got, want, f"d={d} {shape} c={causal} t={tile}")
+
+
+@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("tile", [1024, 64])
+def test_decode_head_dims(d, tile):
+    note(f"decode d={d} tile={tile}")
+    inp = workloads.make_dense(4, 32, 8, 1, 3000, d, seed=77 + d, kv_len="random", sink=True,
+                               nan_pad=True)
+    got = run_dense(inp, tile=tile, decode=True)
+    assert_close(got, oracle_dense(inp), f"decode d={d} tile={tile}")
+
+
+@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_paged_head_dims(d, causal):
+    note(f"paged d={d} causal={causal}")
+    w = workloads.make_paged(B=4, Hq=16, Hkv=4, d=d, q_lens=[1, 40, 7, 90],
+                             kv_lens=[300, 64, 1000, 777], seed=31 + d)
+    want = _paged_oracle(w, causal=causal)
+    assert_close(_paged_run(w, causal=causal, tile=0), want, f"paged d={d} c={causal}")
+    assert_close(_paged_run(w, causal=causal, tile=128), want, f"paged d={d} c={causal} split")
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 32])

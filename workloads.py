@@ -72,6 +72,18 @@ CASES = {
 PAGED_SEED = 1005
 CHUNKED_SEED = 1006
 
+# The same decode and causal prefill shapes at the other head dims the pages'
+# kernels cover (decode at d = 256, prefill at d = 32); measured beside the
+# named workloads.
+HEAD_DIM_CASES = {
+    "decode_splitkv_d256": DenseCase("decode_splitkv_d256", 16, 32, 8, 1, 8192, 256,
+                                     tile_s_kv=1024, decode=True, seed=1008),
+    "causal_prefill_d32": DenseCase("causal_prefill_d32", 2, 32, 8, 8192, 8192, 32,
+                                    causal=True, seed=1009),
+    "causal_prefill_d256": DenseCase("causal_prefill_d256", 2, 32, 8, 8192, 8192, 256,
+                                     causal=True, seed=1010),
+}
+
 
 def make_dense(B, Hq, Hkv, Sq, Skv, d, seed, *, kv_len=None, sink=False,
                nan_pad=False):

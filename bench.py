@@ -313,6 +313,32 @@ def bench_secondary(args, device, stream):
             "ms": round(ms, 5), "bytes": cb, "flops": cf,
             "tflops": round(cf / (ms * 1e-3) / 1e12, 2),
             "roofline_frac": round(t_roof / (ms * 1e-3), 4)}
+    # paged decode at the split-KV decode shape, plain and with the fused append
+    # of each token's K/V (the token's key row comes from k_new and is written
+    # into its page by the same launch)
+    w = workloads.make_paged_decode()
+    kn, vn, _, _ = workloads.take_new_kv(w)
+    gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
+    kn, vn = kn.to(device), vn.to(device)
+    outd = torch.empty_like(gw["q"])
+    db, _ = paged_work(w)
+    tile = 1024
+    ws = torch.empty(m.workspace_size(1, w["Hq"], w["total_q"], gw["page_table"].shape[1] * 64,
+                                      w["d"], tile), dtype=torch.uint8, device=device)
+    for name, append in (("paged_decode_tile1024", False), ("paged_decode_append_tile1024", True)):
+        def dstep(append=append):
+            if append:
+                m.paged_append(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],
+                               gw["page_table"], gw["kv_len"], kn, vn, max_q_len=1,
+                               scale=w["scale"], tile_s_kv=tile, out=outd, workspace=ws)
+            else:
+                m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],
+                        gw["page_table"], gw["kv_len"], max_q_len=1, scale=w["scale"],
+                        tile_s_kv=tile, out=outd, workspace=ws)
+        ms = time_loop(dstep, steps, warm_steps(dstep, stream), stream)
+        res[name] = {"ms": round(ms, 5), "GB/s": round(db / (ms * 1e-3) / 1e9, 1),
+                     "roofline": roof("hbm", db / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    del gw, kn, vn, ws
     # tiny prefill (launch-bound)
     c, _, g = setup_dense("tiny_prefill", device)
     step, out = prefill_step_fn(g, c, 0)
@@ -343,6 +369,17 @@ def run_only(args, device, stream):
                              gw["page_table"], gw["kv_len"], max_q_len=w["max_q_len"],
                              scale=w["scale"], sink=gw["sink"], tile_s_kv=1024)
         return {"workload": name, "ms": time_loop(fn, args.steps, args.warmup, stream)}
+    if name == "paged_decode_append":
+        w = workloads.make_paged_decode()
+        kn, vn, _, _ = workloads.take_new_kv(w)
+        gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
+        kn, vn = kn.to(device), vn.to(device)
+        m = gqa()
+        fn = lambda: m.paged_append(gw["q"], gw["cu_seqlens_q"], gw["k_cache"],  # noqa: E731
+                                    gw["v_cache"], gw["page_table"], gw["kv_len"], kn, vn,
+                                    max_q_len=1, scale=w["scale"], tile_s_kv=1024)
+        ms = time_loop(fn, args.steps, args.warmup, stream)
+        return {"workload": name, "ms": ms, "GB/s": paged_work(w)[0] / (ms * 1e-3) / 1e9}
     if name == "paged_causal_chunked":
         w = workloads.make_paged_chunked()
         gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
@@ -398,7 +435,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--only", choices=["decode_partial", "shortq_longkv", "causal_prefill",
-                                       "ragged_paged", "paged_causal_chunked", "copy"],
+                                       "ragged_paged", "paged_causal_chunked",
+                                       "paged_decode_append", "copy"],
                     help="profiling aid: time only this workload's kernels and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -24,7 +24,7 @@ from ._lib import (GQAError, GQAInvalidArgument, GQAUnsupported,  # noqa: F401
                    GQAWorkspaceError)
 
 __all__ = ["prefill", "decode_splitkv", "splitkv_partial", "splitkv_merge", "paged",
-           "workspace_size", "n_splits", "GQAError"]
+           "paged_append", "workspace_size", "n_splits", "GQAError"]
 
 
 def _ptr(t):
@@ -167,6 +167,29 @@ def paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, *, max_q_len, s
     (partial states + merge kernel), which spreads long sequences over more
     workgroups.
     """
+    return _paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, None, None,
+                  max_q_len=max_q_len, scale=scale, sink=sink, causal=causal,
+                  page_size=page_size, tile_s_kv=tile_s_kv, out=out, workspace=workspace)
+
+
+def paged_append(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, k_new, v_new, *,
+                 max_q_len, scale=None, sink=None, causal=False, page_size=64, tile_s_kv=0,
+                 out=None, workspace=None):
+    """`paged` with the query tokens' own K/V appended in the same launch.
+
+    k_new / v_new: [total_q, Hkv, d] bf16, packed like q.  Token i of
+    sequence b holds key row kv_len[b] - q_len_b + i: the kernel attends it
+    from k_new / v_new and writes it into that row of the cache pages (which
+    must be allocated in page_table).  kv_len counts the new tokens.  Up to
+    32 query rows per kv head (max_q_len * Hq / Hkv <= 32).
+    """
+    return _paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, k_new, v_new,
+                  max_q_len=max_q_len, scale=scale, sink=sink, causal=causal,
+                  page_size=page_size, tile_s_kv=tile_s_kv, out=out, workspace=workspace)
+
+
+def _paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, k_new, v_new, *, max_q_len,
+           scale, sink, causal, page_size, tile_s_kv, out, workspace):
     _need_dev("q", q, torch.bfloat16)
     _need_dev("k_cache", k_cache, torch.bfloat16)
     _need_dev("v_cache", v_cache, torch.bfloat16)
@@ -192,10 +215,25 @@ def paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, *, max_q_len, s
     workspace = _workspace(q.device, nbytes, workspace)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = _lib.load()
-    _lib.check(lib.gqa_attention_paged(
+    if k_new is None and v_new is None:
+        _lib.check(lib.gqa_attention_paged(
+            _ptr(q), q.stride(0), q.stride(1), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache),
+            k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(page_table),
+            max_pages, _ptr(kv_len), _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv,
+            d, int(page_size), total_q, int(max_q_len), _scale(scale, d), _ptr(sink),
+            int(bool(causal)), int(tile_s_kv), _ptr(workspace), wsb, _stream(q.device)))
+        return out
+    _need_dev("k_new", k_new, torch.bfloat16)
+    _need_dev("v_new", v_new, torch.bfloat16)
+    if k_new is None or v_new is None or k_new.shape != (total_q, Hkv, d) or \
+            v_new.shape != k_new.shape or k_new.stride() != v_new.stride() or k_new.stride(2) != 1:
+        raise ValueError("k_new and v_new must both be [total_q, Hkv, d] with equal strides "
+                         "and a contiguous head dim")
+    _lib.check(lib.gqa_attention_paged_append(
         _ptr(q), q.stride(0), q.stride(1), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache),
         k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), _ptr(page_table),
-        max_pages, _ptr(kv_len), _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv,
-        d, int(page_size), total_q, int(max_q_len), _scale(scale, d), _ptr(sink),
-        int(bool(causal)), int(tile_s_kv), _ptr(workspace), wsb, _stream(q.device)))
+        max_pages, _ptr(kv_len), _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1),
+        _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, d, int(page_size), total_q,
+        int(max_q_len), _scale(scale, d), _ptr(sink), int(bool(causal)), int(tile_s_kv),
+        _ptr(workspace), wsb, _stream(q.device)))
     return out

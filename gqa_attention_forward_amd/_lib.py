@@ -73,7 +73,13 @@ SIGNATURES = {
     "gqa_attention_paged": [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P,
                             _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F, _P,
                             _I32, _I32, _P, ctypes.c_size_t, _P],
+    "gqa_attention_paged_append": [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P,
+                                   _P, _P, _I64, _I64,
+                                   _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                   _F, _P, _I32, _I32, _P, ctypes.c_size_t, _P],
 }
+
+ABI_VERSION = 2
 
 _lib = None
 
@@ -99,8 +105,8 @@ def load() -> ctypes.CDLL:
         fn.argtypes = argtypes
         fn.restype = ctypes.c_int32
     lib.gqa_last_error.restype = ctypes.c_char_p
-    if lib.gqa_abi_version() != 1:
-        raise RuntimeError(f"libgqa ABI version {lib.gqa_abi_version()} != 1")
+    if lib.gqa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libgqa ABI version {lib.gqa_abi_version()} != {ABI_VERSION}")
     _lib = lib
     return lib
 

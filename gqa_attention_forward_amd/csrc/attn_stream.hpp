@@ -121,11 +121,16 @@ attn_stream_kernel(const AttnArgs a) {
   const int rows_total = q_len * G;
   const int row0 = qt * (16 * NQB);
   if (row0 >= rows_total) return;
+  // keys read from the cache: all n, or (append) the n - q_len before the
+  // query tokens' own keys, which come from k_new / v_new after the loop
+  int nl = n;
+  if constexpr (PAGED)
+    if (a.k_new) nl = max(n - q_len, 0);
 
-  int kbeg = 0, kend = n;
+  int kbeg = 0, kend = nl;
   if (a.tile > 0) {
     kbeg = s0 * a.tile;
-    kend = min(n, kbeg + nsp * a.tile);
+    kend = min(nl, kbeg + nsp * a.tile);
   }
   if (a.causal) {
     const int p_last = (min(row0 + 16 * NQB, rows_total) - 1) / G;
@@ -227,7 +232,7 @@ attn_stream_kernel(const AttnArgs a) {
       kp = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)j0 * a.k_ss;
       vp = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)j0 * a.v_ss;
     }
-    const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
+    const uint32_t valid = (uint32_t)min(BK, nl - j0);  // >= 1: tiles start below kend <= nl
     const BufRes kr = make_bufres(kp, (valid - 1u) * kss2 + (uint32_t)D * 2u);
     const BufRes vr = make_bufres(vp, (valid - 1u) * vss2 + (uint32_t)D * 2u);
 #pragma unroll
@@ -248,7 +253,7 @@ attn_stream_kernel(const AttnArgs a) {
       p = which ? a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)j0 * a.v_ss
                 : a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)j0 * a.k_ss;
     }
-    const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
+    const uint32_t valid = (uint32_t)min(BK, nl - j0);  // >= 1: tiles start below kend <= nl
     return make_bufres(p, (valid - 1u) * (which ? vss2 : kss2) + (uint32_t)D * 2u);
   };
   auto load_k = [&](int j0, Tile& t) {
@@ -532,6 +537,63 @@ attn_stream_kernel(const AttnArgs a) {
       }
     }
   keys_done:
+    if constexpr (PAGED) {
+      // append: the query tokens' own keys nl .. n - 1 (at most 32) count
+      // once, in the split holding key n - 1, as one more tile of wave 0,
+      // loaded straight from k_new / v_new (no workgroup reads those cache
+      // rows in this launch); the workgroup of q-tile 0 also writes them
+      // into their cache pages.
+      const int nnew = n - nl;
+      const int s_new = a.tile > 0 ? (n - 1) / a.tile : 0;
+      if (a.k_new && nnew > 0 && s_new >= s0 && s_new < s0 + nsp) {
+        while (cur < s_new - s0) {
+          flush(cur);
+          ++cur;
+        }
+        const int64_t t0 = q_row0 + q_len - nnew;  // packed row of key nl
+        const uint16_t* kn = a.k_new + t0 * a.new_st + (int64_t)g * a.new_sh;
+        const uint16_t* vn = a.v_new + t0 * a.new_st + (int64_t)g * a.new_sh;
+        if (wv == 0) {
+          const uint32_t ns2 = (uint32_t)a.new_st * 2u;
+          const BufRes kr = make_bufres(kn, (uint32_t)(nnew - 1) * ns2 + (uint32_t)D * 2u);
+          const BufRes vr = make_bufres(vn, (uint32_t)(nnew - 1) * ns2 + (uint32_t)D * 2u);
+          Tile tn;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+              tn.k[kb][c] = buf_load16(kr, (uint32_t)(16 * kb + c16) * ns2 + 64u * c + 16u * grp);
+#pragma unroll
+          for (int j = 0; j < VPL; ++j)
+            tn.v[j] = buf_load16(vr, (uint32_t)(lane / DC + j * (64 / DC)) * ns2 +
+                                         16u * (lane % DC));
+          // every key of the tile goes through the mask: key nl + r is
+          // visible up to the row's causal bound, and rows r >= nnew not at all
+          wlo = nl;
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            lim[qb] = a.causal ? min(max(n - q_len + pq[qb] + 1, 0), n) : n;
+          stage_v(tn);
+          compute(nl, tn);
+        }
+        if (qt == 0) {
+          uint16_t* kc = const_cast<uint16_t*>(a.k) + (int64_t)g * a.k_sh;
+          uint16_t* vc = const_cast<uint16_t*>(a.v) + (int64_t)g * a.v_sh;
+          for (int idx = threadIdx.x; idx < 2 * nnew * DC; idx += NW * 64) {
+            const int which = idx >= nnew * DC;
+            const int rem = idx - which * nnew * DC;
+            const int r = rem / DC, ch = rem % DC;
+            const int key = nl + r;
+            const int64_t dst = (int64_t)a.page_table[(int64_t)b * a.max_pages + (key >> 6)] *
+                                    a.kv_sp +
+                                (int64_t)(key & 63) * a.kv_sr + 8 * ch;
+            const int64_t src = (int64_t)r * a.new_st + 8 * ch;
+            *reinterpret_cast<uint4*>((which ? vc : kc) + dst) =
+                *reinterpret_cast<const uint4*>((which ? vn : kn) + src);
+          }
+        }
+      }
+    }
     while (cur < nsp) {
       flush(cur);
       ++cur;

@@ -72,6 +72,13 @@ struct AttnArgs {
   int32_t n_qtiles;   // q-tiles per (b, g)
   int32_t total_q;    // paged: packed query rows (partial-state row = h * total_q + t)
   float scale_log2;   // scale * log2(e), > 0
+  // paged append (stream kernel): the K/V of the query tokens, packed like Q
+  // ([total_q, Hkv, d] by (t, h) strides), or nullptr.  Token i of sequence b
+  // holds key row kv_len_b - q_len_b + i, which the kernel attends from here
+  // and writes into its cache page.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_st, new_sh;
 };
 
 // Raw buffer resource (CDNA: stride 0, no swizzle, third dword 0x00020000).

@@ -426,17 +426,21 @@ gqa_status_t gqa_attention_splitkv_merge(const void* workspace, size_t workspace
   return ok();
 }
 
-gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
-                                 const int32_t* cu_seqlens_q, const void* k_cache,
-                                 const void* v_cache, int64_t kv_stride_page,
-                                 int64_t kv_stride_row, int64_t kv_stride_h,
-                                 const int32_t* page_table, int32_t max_pages_per_seq,
-                                 const int32_t* kv_len, void* o, int64_t o_stride_t,
-                                 int64_t o_stride_h, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
-                                 int32_t page_size, int32_t total_q, int32_t max_q_len,
-                                 float scale, const float* sink, int32_t causal,
-                                 int32_t tile_s_kv, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gqa_attention_paged and gqa_attention_paged_append (k_new == nullptr: no append)
+gqa_status_t paged_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                        const int32_t* cu_seqlens_q, const void* k_cache, const void* v_cache,
+                        int64_t kv_stride_page, int64_t kv_stride_row, int64_t kv_stride_h,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        const int32_t* kv_len, const void* k_new, const void* v_new,
+                        int64_t new_stride_t, int64_t new_stride_h, void* o, int64_t o_stride_t,
+                        int64_t o_stride_h, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                        int32_t page_size, int32_t total_q, int32_t max_q_len, float scale,
+                        const float* sink, int32_t causal, int32_t tile_s_kv, void* workspace,
+                        size_t workspace_bytes, void* stream, bool append) {
   if (B < 0 || total_q < 0 || max_q_len < 0 || max_pages_per_seq < 0)
     return fail(GQA_ERR_INVALID_ARGUMENT, "B, total_q, max_q_len and max_pages_per_seq must be >= 0");
   GQA_TRY(check_heads(Hq, Hkv, d));
@@ -444,7 +448,18 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
   GQA_TRY(check_scale(scale));
   if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   GQA_TRY(check_tile(tile_s_kv, false));
+  if (append && (int64_t)max_q_len * (Hq / Hkv) > 32)
+    return fail(GQA_ERR_UNSUPPORTED,
+                "append handles up to 32 query rows per kv head (max_q_len %d x group %d)",
+                max_q_len, Hq / Hkv);
   if (B == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (append) {
+    GQA_TRY(check_ptr("k_new", k_new));
+    GQA_TRY(check_ptr("v_new", v_new));
+    const int64_t ns[2] = {new_stride_t, new_stride_h};
+    GQA_TRY(check_strides("k_new/v_new", ns, 2));
+    GQA_TRY(check_key_stride("k_new/v_new", new_stride_t));
+  }
   GQA_TRY(check_ptr("q", q));
   GQA_TRY(check_ptr("o", o));
   GQA_TRY(check_ptr("k_cache", k_cache));
@@ -486,6 +501,12 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
   a.total_q = total_q;
   a.causal = causal;
   a.scale_log2 = scale * gqa::kLog2e;
+  if (append) {
+    a.k_new = reinterpret_cast<const uint16_t*>(k_new);
+    a.v_new = reinterpret_cast<const uint16_t*>(v_new);
+    a.new_st = new_stride_t;
+    a.new_sh = new_stride_h;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t rows = (int64_t)max_q_len * a.G;
   if (tile_s_kv == 0) {
@@ -505,6 +526,44 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
   const int64_t mo[3] = {0, o_stride_h, o_stride_t};
   GQA_TRY(launch_merge(workspace, o, mo, 1, Hq, total_q, d, (int32_t)n_split, sink, st));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                                 const int32_t* cu_seqlens_q, const void* k_cache,
+                                 const void* v_cache, int64_t kv_stride_page,
+                                 int64_t kv_stride_row, int64_t kv_stride_h,
+                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                 const int32_t* kv_len, void* o, int64_t o_stride_t,
+                                 int64_t o_stride_h, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                 int32_t page_size, int32_t total_q, int32_t max_q_len,
+                                 float scale, const float* sink, int32_t causal,
+                                 int32_t tile_s_kv, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return paged_impl(q, q_stride_t, q_stride_h, cu_seqlens_q, k_cache, v_cache, kv_stride_page,
+                    kv_stride_row, kv_stride_h, page_table, max_pages_per_seq, kv_len, nullptr,
+                    nullptr, 0, 0, o, o_stride_t, o_stride_h, B, Hq, Hkv, d, page_size, total_q,
+                    max_q_len, scale, sink, causal, tile_s_kv, workspace, workspace_bytes, stream,
+                    false);
+}
+
+gqa_status_t gqa_attention_paged_append(
+    const void* q, int64_t q_stride_t, int64_t q_stride_h, const int32_t* cu_seqlens_q,
+    void* k_cache, void* v_cache, int64_t kv_stride_page, int64_t kv_stride_row,
+    int64_t kv_stride_h, const int32_t* page_table, int32_t max_pages_per_seq,
+    const int32_t* kv_len, const void* k_new, const void* v_new, int64_t new_stride_t,
+    int64_t new_stride_h, void* o, int64_t o_stride_t, int64_t o_stride_h, int32_t B, int32_t Hq,
+    int32_t Hkv, int32_t d, int32_t page_size, int32_t total_q, int32_t max_q_len, float scale,
+    const float* sink, int32_t causal, int32_t tile_s_kv, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return paged_impl(q, q_stride_t, q_stride_h, cu_seqlens_q, k_cache, v_cache, kv_stride_page,
+                    kv_stride_row, kv_stride_h, page_table, max_pages_per_seq, kv_len, k_new,
+                    v_new, new_stride_t, new_stride_h, o, o_stride_t, o_stride_h, B, Hq, Hkv, d,
+                    page_size, total_q, max_q_len, scale, sink, causal, tile_s_kv, workspace,
+                    workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 1
+#define GQA_ABI_VERSION 2
 
 typedef int32_t gqa_status_t;
 
@@ -212,6 +212,41 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
                                  int32_t max_q_len, float scale, const float* sink,
                                  int32_t causal, int32_t tile_s_kv, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_attention_paged with the query tokens' own K/V appended in the same
+ * launch (AstrAI commit log, the paged decode fix: the decode kernel takes
+ * the newest tokens' K/V from separate new-K/new-V pointers instead of the
+ * cache).  Besides the gqa_attention_paged arguments:
+ *
+ *  k_new / v_new : bf16 [total_q, Hkv, d] packed like q, strides (t, h) in
+ *                 elements (new_stride_t, new_stride_h; d contiguous; the
+ *                 same strides for both; new_stride_t below 2^26).  Token i of sequence b (row
+ *                 cu_seqlens_q[b] + i) holds key row j = kv_len[b] - q_len_b
+ *                 + i of that sequence: kv_len counts the new tokens, and
+ *                 kv_len[b] >= q_len_b (tokens that would land before key
+ *                 row 0 are dropped).
+ *  k_cache / v_cache : written as well as read: each row j above is stored
+ *                 into page page_table[b, j / 64], in-page row j % 64, kv head
+ *                 g, so the page must be allocated in page_table.  No other
+ *                 cache row is written.  The cache must not overlap k_new,
+ *                 v_new, q or o.
+ *
+ * The output equals writing those rows into the cache first and then calling
+ * gqa_attention_paged; the attention reads them from k_new / v_new, so no
+ * cache row is read and written in the same launch.  Supported for up to 32
+ * query rows per kv head: max_q_len * (Hq / Hkv) <= 32 (decode and short
+ * query blocks; the stream kernel), else GQA_ERR_UNSUPPORTED.
+ */
+gqa_status_t gqa_attention_paged_append(
+    const void* q, int64_t q_stride_t, int64_t q_stride_h, const int32_t* cu_seqlens_q,
+    void* k_cache, void* v_cache, int64_t kv_stride_page, int64_t kv_stride_row,
+    int64_t kv_stride_h, const int32_t* page_table, int32_t max_pages_per_seq,
+    const int32_t* kv_len, const void* k_new, const void* v_new, int64_t new_stride_t,
+    int64_t new_stride_h, void* o, int64_t o_stride_t, int64_t o_stride_h, int32_t B, int32_t Hq,
+    int32_t Hkv, int32_t d, int32_t page_size, int32_t total_q, int32_t max_q_len, float scale,
+    const float* sink, int32_t causal, int32_t tile_s_kv, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

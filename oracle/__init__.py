@@ -10,7 +10,8 @@ Every function here is the plain (non-online) definition written out in
 float64, following the pages cited in each docstring:
 
 * AstrAI commit log (gitea, ViperEkura/AstrAI) -- the commit that packs
-  HB = min(G, warps) query heads per block and the paged-attention commits;
+  HB = min(G, warps) query heads per block, the paged-attention commits and
+  the paged decode fix (new-K / new-V pointers for the newest tokens);
 * kernbench2 commit log, src/kernbench/benches (git.ywkang.dev) -- the
   tile-granular ring-KV commit (persistent (m, l, O) state, TILE_S_KV) and
   the 2-D mesh all-reduce-mlo commit (associativity of the merge);
@@ -33,4 +34,5 @@ from .attention import (  # noqa: F401
     gather_paged_fp64,
     paged_attention_fp64,
     paged_attention_rows_fp64,
+    paged_append_fp64,
 )

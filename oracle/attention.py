@@ -318,6 +318,39 @@ def paged_attention_fp64(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, 
     return out
 
 
+def paged_append_fp64(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, k_new, v_new, *,
+                      scale: float, page_size: int, sink=None, causal: bool = False):
+    """Append form of `paged_attention_fp64`: the query tokens bring their own K/V.
+
+    AstrAI commit log, the paged decode fix (the decode kernel reads the
+    newest tokens' K/V through separate new-K / new-V pointers rather than
+    from the cache).  Token i of sequence b (packed row cu[b] + i) holds key
+    row j = kv_len[b] - q_len_b + i of that sequence; a token with j < 0 is
+    dropped.  The rows are stored into copies of the pools first (page
+    page_table[b, j // page_size], in-page row j % page_size), then the
+    attention is exactly `paged_attention_fp64` over those copies.
+    Returns (out [total_q, Hq, d], k_cache', v_cache').
+    """
+    kc = _f64(k_cache).copy()
+    vc = _f64(v_cache).copy()
+    kn, vn = _f64(k_new), _f64(v_new)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    pt = np.asarray(page_table, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        qlen = int(cu[b + 1] - cu[b])
+        n = int(kv_len[b])
+        for i in range(qlen):
+            j = n - qlen + i
+            if j < 0:
+                continue
+            page = pt[b, j // page_size]
+            kc[page, j % page_size] = kn[cu[b] + i]
+            vc[page, j % page_size] = vn[cu[b] + i]
+    out = paged_attention_fp64(q, cu, kc, vc, page_table, kv_len, scale=scale,
+                               page_size=page_size, sink=sink, causal=causal)
+    return out, kc, vc
+
+
 def paged_attention_rows_fp64(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, t_idx,
                               h_idx, *, scale: float, page_size: int, sink=None,
                               causal: bool = False) -> np.ndarray:

@@ -100,6 +100,22 @@ int main(void) {
          gqa_attention_paged(P, 4096, 128, P, P, P, 8192, 128, 128, P, 64, P, P, 4096, 128, 8, 32,
                              1, 128, 64, 100, 64, 0.088f, NULL, 0, 100, P, 1 << 30, NULL),
          GQA_ERR_INVALID_ARGUMENT);
+  /* append: B 8, Hq 32, Hkv 8 (G 4), d 128, total_q 8, max_q_len mq */
+#define APPEND(kn, vn, nst, mq) \
+  gqa_attention_paged_append(P, 4096, 128, P, P, P, 8192, 128, 128, P, 64, P, kn, vn, nst, 128, \
+                             P, 4096, 128, 8, 32, 8, 128, 64, 8, mq, 0.088f, NULL, 0, 0, NULL, 0, \
+                             NULL)
+  expect("append NULL k_new", APPEND(NULL, P, 1024, 1), GQA_ERR_INVALID_ARGUMENT);
+  expect("append NULL v_new", APPEND(P, NULL, 1024, 1), GQA_ERR_INVALID_ARGUMENT);
+  expect("append misaligned k_new", APPEND(M, P, 1024, 1), GQA_ERR_UNSUPPORTED);
+  expect("append new stride 1020", APPEND(P, P, 1020, 1), GQA_ERR_UNSUPPORTED);
+  expect("append 36 rows per kv head", APPEND(P, P, 1024, 9), GQA_ERR_UNSUPPORTED);
+  expect("append new stride 2^26", APPEND(P, P, (int64_t)1 << 26, 1), GQA_ERR_UNSUPPORTED);
+  expect("append empty batch",
+         gqa_attention_paged_append(NULL, 0, 0, NULL, NULL, NULL, 0, 0, 0, NULL, 0, NULL, NULL,
+                                    NULL, 0, 0, NULL, 0, 0, 0, 32, 8, 128, 64, 0, 0, 0.088f, NULL,
+                                    0, 0, NULL, 0, NULL),
+         GQA_OK);
   printf("%s\n", failures ? "FAILED" : "ALL OK");
   return failures ? 1 : 0;
 }

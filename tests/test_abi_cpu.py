@@ -19,7 +19,7 @@ def test_library_loads_and_exports_header_symbols():
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"{name} has no ctypes signature"
-    assert lib.gqa_abi_version() == 1
+    assert lib.gqa_abi_version() == _lib.ABI_VERSION == 2
 
 
 def test_workspace_size_matches_layout():

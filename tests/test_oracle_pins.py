@@ -430,6 +430,46 @@ def test_row_subsets_match_full():
     np.testing.assert_allclose(pr, pf[t_idx, h_idx], rtol=1e-13, atol=1e-15)
 
 
+def test_paged_append_equals_attention_over_the_full_cache():
+    """The append form stores each token's K/V at key row kv_len - q_len + i:
+    with those rows cut out of a pool (NaN in their place) and handed in as
+    k_new / v_new, it must give back the original pool and exactly the
+    attention over it (any wrong row or token index leaves a NaN hole or
+    moves a key)."""
+    f = workloads.to_f64
+    for causal in (False, True):
+        w = workloads.make_paged(B=4, Hq=8, Hkv=2, d=16, q_lens=[1, 3, 1, 5],
+                                 kv_lens=[1, 70, 128, 129], seed=9)
+        kn, vn, kh, vh = workloads.take_new_kv(w)
+        assert torch.isnan(kh.float()).any()
+        args = dict(scale=w["scale"], page_size=64, sink=f(w["sink"]), causal=causal)
+        want = oracle.paged_attention_fp64(f(w["q"]), w["cu_seqlens_q"], f(w["k_cache"]),
+                                           f(w["v_cache"]), w["page_table"], w["kv_len"], **args)
+        got, kc, vc = oracle.paged_append_fp64(f(w["q"]), w["cu_seqlens_q"], f(kh), f(vh),
+                                               w["page_table"], w["kv_len"], f(kn), f(vn), **args)
+        np.testing.assert_array_equal(got, want)
+        np.testing.assert_array_equal(kc, f(w["k_cache"]))
+        np.testing.assert_array_equal(vc, f(w["v_cache"]))
+
+
+def test_paged_append_drops_tokens_before_row_zero():
+    """kv_len 2 with 3 query tokens: token 0 would be key row -1 and is dropped;
+    tokens 1 and 2 become key rows 0 and 1 (checked against the plain
+    definition over those two keys)."""
+    rng = np.random.default_rng(4)
+    q, kn, vn = rng.standard_normal((3, 2, 8)), rng.standard_normal((3, 1, 8)), \
+        rng.standard_normal((3, 1, 8))
+    kc = np.full((2, 64, 1, 8), np.nan)
+    vc = np.full((2, 64, 1, 8), np.nan)
+    out, kc2, _ = oracle.paged_append_fp64(q, [0, 3], kc, vc, [[1, 0]], [2], kn, vn, scale=0.5,
+                                           page_size=64)
+    np.testing.assert_array_equal(kc2[1, :2, 0], kn[1:, 0])
+    assert np.isnan(kc2[1, 2:]).all() and np.isnan(kc2[0]).all()
+    want = oracle.attention_fp64(q.transpose(1, 0, 2)[None], kn[1:].transpose(1, 0, 2)[None],
+                                 vn[1:].transpose(1, 0, 2)[None], scale=0.5)
+    np.testing.assert_array_equal(out, want[0].transpose(1, 0, 2))
+
+
 # ---------------------------------------------------------------- workloads
 
 def test_workloads_deterministic_and_structured():

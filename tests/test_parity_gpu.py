@@ -173,6 +173,65 @@ def test_paged_causal_chunked_full(tile):
     assert_close(out[t, h], want, f"paged causal chunked full tile={tile}")
 
 
+# paged append (the query tokens' K/V handed in beside the cache and written
+# into it by the same launch): B, Hq, Hkv, d, q_lens, kv_lens
+APPEND_CASES = [
+    (6, 32, 8, 128, [1] * 6, [1, 63, 64, 65, 1000, 4096]),   # decode, G = 4
+    (4, 32, 1, 128, [1] * 4, [5, 700, 2049, 3000]),          # G = 32: two 16-column blocks
+    (4, 16, 4, 64, [1, 2, 5, 8], [8, 64, 200, 1030]),        # short query blocks
+    (3, 8, 4, 256, [1, 4, 16], [16, 300, 2000]),             # d = 256, 32 rows: two q-tiles
+    (3, 8, 8, 32, [1, 7, 20], [20, 90, 700]),                # d = 32, G = 1
+]
+
+
+@pytest.mark.parametrize("case", range(len(APPEND_CASES)))
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tile", [0, 64, 1024])
+def test_paged_append(case, causal, tile):
+    B, Hq, Hkv, d, q_lens, kv_lens = APPEND_CASES[case]
+    note(f"paged append case={APPEND_CASES[case]} causal={causal} tile={tile}")
+    w = workloads.make_paged(B=B, Hq=Hq, Hkv=Hkv, d=d, q_lens=q_lens, kv_lens=kv_lens,
+                             seed=40 + case)
+    kn, vn, kh, vh = workloads.take_new_kv(w)
+    g = to_dev(w)
+    kc, vc = kh.to(dev()), vh.to(dev())
+    out = gqa().paged_append(g["q"], g["cu_seqlens_q"], kc, vc, g["page_table"], g["kv_len"],
+                             kn.to(dev()), vn.to(dev()), max_q_len=w["max_q_len"],
+                             scale=w["scale"], sink=g["sink"], causal=causal, tile_s_kv=tile)
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().numpy(), _paged_oracle(w, causal=causal),
+                 f"append case={case} c={causal} t={tile}")
+    # the holes are filled with exactly the new rows; nothing else changed
+    assert torch.equal(kc.cpu().view(torch.int16), w["k_cache"].view(torch.int16))
+    assert torch.equal(vc.cpu().view(torch.int16), w["v_cache"].view(torch.int16))
+
+
+def test_paged_append_decode_full_size():
+    """The timed append workload (16 sequences of 8192 keys, Hq 32, Hkv 8,
+    splits of 1024): sampled rows against the oracle over the full cache,
+    and the cache rows restored bit for bit."""
+    note("paged append decode, full size, tile=1024")
+    w = workloads.make_paged_decode()
+    kn, vn, kh, vh = workloads.take_new_kv(w)
+    g = to_dev(w)
+    kc, vc = kh.to(dev()), vh.to(dev())
+    out = gqa().paged_append(g["q"], g["cu_seqlens_q"], kc, vc, g["page_table"], g["kv_len"],
+                             kn.to(dev()), vn.to(dev()), max_q_len=1, scale=w["scale"],
+                             tile_s_kv=1024)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    t = np.repeat(np.arange(w["B"]), 4)
+    h = np.random.default_rng(3).integers(0, w["Hq"], t.size)
+    want = oracle.paged_attention_rows_fp64(w["q"].float().numpy(), w["cu_seqlens_q"].numpy(),
+                                            w["k_cache"].float().numpy(),
+                                            w["v_cache"].float().numpy(), w["page_table"].numpy(),
+                                            w["kv_len"].numpy(), t, h, scale=w["scale"],
+                                            page_size=64)
+    assert_close(out[t, h], want, "paged append decode full size")
+    assert torch.equal(kc.cpu().view(torch.int16), w["k_cache"].view(torch.int16))
+    assert torch.equal(vc.cpu().view(torch.int16), w["v_cache"].view(torch.int16))
+
+
 @pytest.mark.parametrize("G", [4, 32])
 @pytest.mark.parametrize("tile", [0, 1024])
 def test_paged_decode_shape(G, tile):

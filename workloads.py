@@ -193,6 +193,38 @@ def make_paged_chunked(B=8, Hq=32, Hkv=1, d=128, *, chunk=512, max_prefix=3584,
                       q_lens=[chunk] * B, kv_lens=(prefix + chunk).tolist())
 
 
+def make_paged_decode(B=16, Hq=32, Hkv=8, d=128, kv=8192, seed=1011):
+    """The split-KV decode shape over a paged pool: one query token per
+    sequence, every sequence kv keys long (the token's own key included)."""
+    return make_paged(B, Hq, Hkv, d, q_lens=[1] * B, kv_lens=[kv] * B, seed=seed, sink=False)
+
+
+def take_new_kv(w):
+    """Append-form inputs from a paged workload: the K/V rows of every query
+    token (token i of sequence b is key row kv_len[b] - q_len_b + i) are
+    copied out of the pools into packed [total_q, Hkv, d] tensors, and those
+    cache rows are set to NaN.  Requires kv_len[b] >= q_len_b.
+    Returns (k_new, v_new, k_cache_with_holes, v_cache_with_holes)."""
+    cu = w["cu_seqlens_q"].numpy().astype(np.int64)
+    pt = w["page_table"].numpy().astype(np.int64)
+    kv_len = w["kv_len"].numpy().astype(np.int64)
+    ps = w["page_size"]
+    kc, vc = w["k_cache"].clone(), w["v_cache"].clone()
+    k_new = torch.empty((w["total_q"],) + tuple(kc.shape[2:]), dtype=kc.dtype)
+    v_new = torch.empty_like(k_new)
+    for b in range(len(cu) - 1):
+        qlen = int(cu[b + 1] - cu[b])
+        assert kv_len[b] >= qlen, "each sequence's keys must include its query tokens"
+        for i in range(qlen):
+            j = int(kv_len[b]) - qlen + i
+            page, row = int(pt[b, j // ps]), j % ps
+            k_new[cu[b] + i] = kc[page, row]
+            v_new[cu[b] + i] = vc[page, row]
+            kc[page, row] = float("nan")
+            vc[page, row] = float("nan")
+    return k_new, v_new, kc, vc
+
+
 def to_f64(t) -> np.ndarray:
     """Exact float64 copy of a CPU tensor (bf16 and f32 promote exactly)."""
     if t is None:

@@ -68,11 +68,18 @@ struct PrefillCfg {
 
 constexpr float kLazyRescale = 8.f;  // log2 units
 
+// Row maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950):
+// fmaxf would first quiet each input with an extra instruction.  The scores
+// are never NaN (padding rows read as zero and masked keys are -inf).
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // max / sum of x over lanes l and l ^ 32
 __device__ __forceinline__ float half_swap_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_swap_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -310,25 +317,29 @@ attn_prefill_kernel(const AttnArgs a) {
     }
     float m = s[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) m = fmaxf(m, s[j]);
+    for (int j = 1; j < 16; ++j) m = vmax(m, s[j]);
     const float mx = half_swap_max(m) * a.scale_log2;
     mtrue = fmaxf(mtrue, mx);
     const bool move = mx > mref + kLazyRescale;
     const float alpha = move ? ex2(mref - mx) : 1.f;  // 0 when mref = -inf
     mref = move ? mx : mref;
     const float mu = (mref == -INFINITY) ? 0.f : mref;
+    // each pair of weights is rounded once (one v_cvt_pk_bf16_f32) and that
+    // packed word feeds both the row sum and the P operand
     float ls = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        bf16x2 pp;
-        pp[0] = (__bf16)ex2(__builtin_fmaf(s[8 * t + e], a.scale_log2, -mu));
-        pp[1] = (__bf16)ex2(__builtin_fmaf(s[8 * t + e + 1], a.scale_log2, -mu));
-        pb[t][e] = pp[0];
-        pb[t][e + 1] = pp[1];
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 x = {ex2(__builtin_fmaf(s[8 * t + 2 * e], a.scale_log2, -mu)),
+                         ex2(__builtin_fmaf(s[8 * t + 2 * e + 1], a.scale_log2, -mu))};
+        const bf16x2 pp = __builtin_convertvector(x, bf16x2);
         ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
+        w[e] = __builtin_bit_cast(uint32_t, pp);
       }
+      pb[t] = __builtin_bit_cast(bf16x8, w);
+    }
     l = l * alpha + ls;
     return alpha;
   };
@@ -394,10 +405,13 @@ attn_prefill_kernel(const AttnArgs a) {
 
   using True = std::integral_constant<bool, true>;
   using False = std::integral_constant<bool, false>;
-  auto step_early = [&](auto mask_tag, int it) {
+  // `par` is the tile's LDS stage (it & 1) as a constant, so every LDS
+  // address of the step is a base register plus an immediate
+  auto step_early = [&](auto mask_tag, int it, auto par) {
+    constexpr int PAR = decltype(par)::value;
     const int j0 = kbeg + it * BK;
     load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
-    const uint16_t* Ks = smem + (it & 1) * C::STAGE;
+    const uint16_t* Ks = smem + PAR * C::STAGE;
     const uint16_t* Vs = Ks + C::KTILE;
     bf16x8 k0[NCK], k1[NCK], v0[2 * NDB], v1[2 * NDB], p0[2], p1[2];
     kfetch(Ks, 0, k0);
@@ -422,7 +436,7 @@ attn_prefill_kernel(const AttnArgs a) {
     rescale(alpha1);
     // 4. stage the next tile into the idle buffer (no wave reads it before
     // the barrier below), then O += V_1 P_1: the LDS writes overlap the MFMAs
-    store_tile((it + 1) & 1, nx);
+    store_tile(1 - PAR, nx);
     pv_reg(v1, p1, std::integral_constant<int, 2>{});
     lds_barrier();
   };
@@ -457,8 +471,28 @@ attn_prefill_kernel(const AttnArgs a) {
 
   int it = 0;
   if constexpr (EARLY) {
-    for (; it < nfull; ++it) step_early(False{}, it);
-    for (; it < ntiles; ++it) step_early(True{}, it);
+    // Tiles two at a time (stages 0 and 1), unmasked tiles first, then the
+    // masked ones; a leftover single tile runs on its own stage.  (The
+    // smaller forms keep a runtime stage: unrolled, they would spill.)
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    for (; it + 1 < nfull; it += 2) {
+      step_early(False{}, it, P0{});
+      step_early(False{}, it + 1, P1{});
+    }
+    if (it < nfull) {  // odd number of unmasked tiles
+      step_early(False{}, it, P0{});
+      ++it;
+      if (it < ntiles) {
+        step_early(True{}, it, P1{});
+        ++it;
+      }
+    }
+    for (; it + 1 < ntiles; it += 2) {
+      step_early(True{}, it, P0{});
+      step_early(True{}, it + 1, P1{});
+    }
+    if (it < ntiles) step_early(True{}, it, P0{});
   } else {
     for (; it < nfull; ++it) step(False{}, it);
     for (; it < ntiles; ++it) step(True{}, it);

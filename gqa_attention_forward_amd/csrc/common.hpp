@@ -39,6 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // (1.0, 1.0) in bf16: v_dot2 against it sums a packed pair in fp32
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};

@@ -252,6 +252,23 @@ def bench_secondary(args, device, stream):
         "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2), "flops": fl,
         "roofline": roof("mfma", fl / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s")}
     del g, out
+    # the same decode with the in-kernel merge (one launch; tickets zeroed once)
+    c, _, g = setup_dense("decode_splitkv", device)
+    m = gqa()
+    outf = torch.empty_like(g["q"])
+    wsf = torch.empty(m.workspace_size(c.B, c.Hq, 1, c.Skv, c.d, c.tile_s_kv), dtype=torch.uint8,
+                      device=device)
+    tk = torch.zeros(c.B * c.Hq, dtype=torch.int32, device=device)
+
+    def fstep():
+        m.decode_splitkv(g["q"], g["k"], g["v"], kv_len=g["kv_len"], scale=g["scale"],
+                         tile_s_kv=c.tile_s_kv, out=outf, workspace=wsf, fused=True, tickets=tk)
+    ms = time_loop(fstep, steps, warm_steps(fstep, stream), stream)
+    tb, _ = dense_bytes(c)
+    res["decode_splitkv_fused_merge"] = {
+        "ms": round(ms, 5), "GB/s": round(tb / (ms * 1e-3) / 1e9, 1),
+        "roofline": roof("hbm", tb / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    del g, outf, wsf, tk
     # the other head dims: decode at d = 256, causal prefill at d = 32 and 256
     c, _, g = setup_dense("decode_splitkv_d256", device)
     step, _, _, _ = decode_step_fns(g, c)

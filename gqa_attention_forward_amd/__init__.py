@@ -99,8 +99,17 @@ def prefill(q, k, v, *, kv_len=None, scale=None, sink=None, causal=False, tile_s
 
 
 def decode_splitkv(q, k, v, *, kv_len=None, scale=None, sink=None, tile_s_kv=1024, out=None,
-                   workspace=None):
-    """Single-token decode: q [B, Hq, 1, d]; split-KV partials then the merge kernel."""
+                   workspace=None, fused=False, tickets=None):
+    """Single-token decode: q [B, Hq, 1, d]; split-KV partials then the merge kernel.
+
+    fused=True merges the partials inside the partial kernel (one launch).
+    It takes `tickets`, an int32 device tensor of at least B * Hq entries
+    that is zero before its first use and is left zero by every call (a
+    zeroed one is allocated per call when none is given).
+    """
+    if fused:
+        return _decode_fused(q, k, v, kv_len=kv_len, scale=scale, sink=sink,
+                             tile_s_kv=tile_s_kv, out=out, workspace=workspace, tickets=tickets)
     _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
     _need_dev("kv_len", kv_len, torch.int32)
     _need_dev("sink", sink, torch.float32)
@@ -119,6 +128,33 @@ def decode_splitkv(q, k, v, *, kv_len=None, scale=None, sink=None, tile_s_kv=102
         _ptr(v), _lib.strides3(v.stride()[:3]), _ptr(out), _lib.strides3(out.stride()[:3]),
         B, Hq, Hkv, Skv, d, _ptr(kv_len), _scale(scale, d), _ptr(sink), int(tile_s_kv),
         _ptr(workspace), wsb, _stream(q.device)))
+    return out
+
+
+def _decode_fused(q, k, v, *, kv_len, scale, sink, tile_s_kv, out, workspace, tickets):
+    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
+    _need_dev("kv_len", kv_len, torch.int32)
+    _need_dev("sink", sink, torch.float32)
+    _need_dev("tickets", tickets, torch.int32)
+    B, Hq, Sq, d = q.shape
+    if Sq != 1:
+        raise ValueError("decode_splitkv takes one query row per (b, h)")
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if tickets is None:
+        tickets = torch.zeros(B * Hq, dtype=torch.int32, device=q.device)
+    if not tickets.is_contiguous():
+        raise ValueError("tickets must be a contiguous int32 tensor")
+    nbytes = workspace_size(B, Hq, 1, Skv, d, tile_s_kv)
+    workspace = _workspace(q.device, nbytes, workspace)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = _lib.load()
+    _lib.check(lib.gqa_attention_decode_splitkv_fused(
+        _ptr(q), _lib.strides3(q.stride()[:3]), _ptr(k), _lib.strides3(k.stride()[:3]),
+        _ptr(v), _lib.strides3(v.stride()[:3]), _ptr(out), _lib.strides3(out.stride()[:3]),
+        B, Hq, Hkv, Skv, d, _ptr(kv_len), _scale(scale, d), _ptr(sink), int(tile_s_kv),
+        _ptr(workspace), wsb, _ptr(tickets), tickets.numel(), _stream(q.device)))
     return out
 
 

@@ -624,10 +624,97 @@ attn_stream_kernel(const AttnArgs a) {
         row = ((int64_t)b * a.Hq + h) * a.Sq + p;
       const int64_t idx = row * a.n_split + s0 + s;
       const float* pc = pend + ((s * NQB + qb) * 16 + col) * C::PSTR;
-      if (ln < LPC)
-        *reinterpret_cast<float4*>(a.ws_o + idx * D + 4 * ln) =
-            *reinterpret_cast<const float4*>(pc + 4 * ln);
-      if (ln == 0) a.ws_ml[idx] = *reinterpret_cast<const float2*>(pc + D);
+      if (a.tickets) {
+        // in-kernel merge: system-scope stores go through to memory, which
+        // leaves the device-scope release below less to write back
+        if (ln < LPC)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(a.ws_o + idx * D + 4 * ln) + e,
+                               __float_as_uint(pc[4 * ln + e]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        if (ln == 0)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(a.ws_ml + idx) + e,
+                               __float_as_uint(pc[D + e]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+      } else {
+        if (ln < LPC)
+          *reinterpret_cast<float4*>(a.ws_o + idx * D + 4 * ln) =
+              *reinterpret_cast<const float4*>(pc + 4 * ln);
+        if (ln == 0) a.ws_ml[idx] = *reinterpret_cast<const float2*>(pc + D);
+      }
+    }
+
+    // ---- in-kernel merge.  The pattern is the AstrAI commit log's scale-ring
+    // epilogue (after a fence, a counter elects the last block, which
+    // finishes the reduction in the same launch).  Here every lane's partial
+    // stores are released device-wide, each workgroup takes a ticket for its
+    // (b, kv head, q-tile), and the one that draws the last of the n_sg
+    // tickets acquires the others' partials, merges every split of its rows
+    // (the merge kernel's arithmetic, sink included) and resets the ticket.
+    // No workgroup waits on another.
+    if (a.tickets) {
+      // The barrier makes every wave's stores visible to thread 0, whose
+      // device-scope fences then release them (and, for the last workgroup,
+      // acquire the others' partials) for the whole workgroup: on gfx950 a
+      // device-scope release writes back the XCD's L2, so one per workgroup.
+      __syncthreads();
+      int* flag = reinterpret_cast<int*>(slots);
+      if (threadIdx.x == 0) {
+        int32_t* tk = a.tickets + (int64_t)bg * a.n_qtiles + qt;
+        __threadfence();
+        const int last = atomicAdd(tk, 1) == n_sg - 1;
+        if (last) {
+          atomicExch(tk, 0);
+          __threadfence();
+        }
+        *flag = last;
+      }
+      __syncthreads();
+      if (*flag == 0) return;
+      for (int it = CPI * wv + half; it < NQB * 16; it += CPI * NW) {
+        const int rho = row0 + it;
+        if (rho >= rows_total) continue;
+        const int p = rho / G, h = g * G + (rho - p * G);
+        int64_t row;
+        if constexpr (PAGED)
+          row = (int64_t)h * a.total_q + q_row0 + p;
+        else
+          row = ((int64_t)b * a.Hq + h) * a.Sq + p;
+        const float2* ml = a.ws_ml + row * a.n_split;
+        const float* ot = a.ws_o + row * a.n_split * D + 4 * ln;
+        const float sk = a.sink ? a.sink[h] : -INFINITY;  // scaled domain, natural log
+        float M = sk;
+        for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, ml[sp].x);
+        float L = sk == -INFINITY ? 0.f : __expf(sk - M);
+        float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (M != -INFINITY) {
+          for (int sp = 0; sp < a.n_split; ++sp) {
+            const float2 st = ml[sp];
+            if (st.x == -INFINITY) continue;  // empty split: weight 0
+            const float w = __expf(st.x - M);
+            L += st.y * w;
+            if (ln < LPC) {
+              const float4 ov = *reinterpret_cast<const float4*>(ot + (int64_t)sp * D);
+              o4.x += w * ov.x;
+              o4.y += w * ov.y;
+              o4.z += w * ov.z;
+              o4.w += w * ov.w;
+            }
+          }
+        }
+        const float inv = (M != -INFINITY && L > 0.f) ? 1.f / L : 0.f;
+        uint16_t* op;
+        if constexpr (PAGED)
+          op = a.o + (int64_t)(q_row0 + p) * a.o_ss + (int64_t)h * a.o_sh;
+        else
+          op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)p * a.o_ss;
+        if (ln < LPC)
+          *reinterpret_cast<uint2*>(op + 4 * ln) =
+              make_uint2(pack_bf16x2(o4.x * inv, o4.y * inv), pack_bf16x2(o4.z * inv, o4.w * inv));
+      }
     }
   }
 }

@@ -80,6 +80,9 @@ struct AttnArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   int64_t new_st, new_sh;
+  // in-kernel merge (stream kernel, partial mode): one ticket per (b, kv
+  // head, q-tile), zero on entry and left zero; nullptr = merge kernel
+  int32_t* tickets;
 };
 
 // Raw buffer resource (CDNA: stride 0, no swizzle, third dword 0x00020000).

@@ -389,6 +389,37 @@ gqa_status_t gqa_attention_decode_splitkv(const void* q, const int64_t q_stride[
                                workspace_bytes, stream);
 }
 
+gqa_status_t gqa_attention_decode_splitkv_fused(
+    const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
+    const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3], int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t Skv, int32_t d, const int32_t* kv_len, float scale,
+    const float* sink, int32_t tile_s_kv, void* workspace, size_t workspace_bytes,
+    int32_t* tickets, int64_t n_tickets, void* stream) {
+  GQA_TRY(check_dense(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, 1, Skv, d, scale, 0));
+  GQA_TRY(check_tile(tile_s_kv, true));
+  if (Hq / Hkv > 32)
+    return fail(GQA_ERR_UNSUPPORTED, "in-kernel merge handles groups of up to 32 heads (G = %d)",
+                Hq / Hkv);
+  const int64_t rows = (int64_t)B * Hq;
+  if (rows == 0) return ok();
+  GQA_TRY(check_ptr("o", o));
+  GQA_TRY(check_strides("o", o_stride, 3));
+  if (!tickets) return fail(GQA_ERR_INVALID_ARGUMENT, "tickets is NULL");
+  if (n_tickets < rows)
+    return fail(GQA_ERR_WORKSPACE, "tickets holds %lld entries, needs B * Hq = %lld",
+                (long long)n_tickets, (long long)rows);
+  GQA_TRY(check_workspace(workspace, workspace_bytes,
+                          workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d)));
+  gqa::AttnArgs a = dense_args(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, 1, Skv, kv_len,
+                               scale, 0);
+  a.o = reinterpret_cast<uint16_t*>(o);
+  a.o_sb = o_stride[0]; a.o_sh = o_stride[1]; a.o_ss = o_stride[2];
+  a.sink = sink;
+  a.tickets = tickets;
+  GQA_TRY(run_partial(a, d, tile_s_kv, workspace, reinterpret_cast<hipStream_t>(stream)));
+  return ok();
+}
+
 gqa_status_t gqa_attention_splitkv_partial(const void* q, const int64_t q_stride[3],
                                            const void* k, const int64_t k_stride[3],
                                            const void* v, const int64_t v_stride[3], int32_t B,

@@ -148,6 +148,31 @@ gqa_status_t gqa_attention_decode_splitkv(const void* q, const int64_t q_stride[
                                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_attention_decode_splitkv in one launch: the split-KV partial states
+ * are merged inside the partial kernel instead of by a second kernel.  The
+ * pattern is the AstrAI commit log's scale-ring epilogue (after a fence, a
+ * counter elects the last block, which finishes the reduction with no extra
+ * launch).  Each workgroup writes its partial states, releases them
+ * device-wide and takes a ticket for its (b, kv head, q-tile); the workgroup
+ * that draws the last ticket merges every split of those rows exactly as the
+ * merge kernel does (sink included, one normalisation) and resets the
+ * ticket.  Same arguments as gqa_attention_decode_splitkv, plus:
+ *
+ *  tickets   : device int32 array of n_tickets >= B * Hq entries, all ZERO
+ *              before the first call; every call leaves them zero.  Calls
+ *              that overlap in time must not share it (nor the workspace).
+ *              Too few entries: GQA_ERR_WORKSPACE.
+ *
+ * Group sizes G = Hq / Hkv up to 32, else GQA_ERR_UNSUPPORTED.
+ */
+gqa_status_t gqa_attention_decode_splitkv_fused(
+    const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
+    const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3], int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t Skv, int32_t d, const int32_t* kv_len, float scale,
+    const float* sink, int32_t tile_s_kv, void* workspace, size_t workspace_bytes,
+    int32_t* tickets, int64_t n_tickets, void* stream);
+
+/*
  * The two phases of split-KV on their own, for callers that place the
  * partial states themselves (for instance KV sharded across devices, with
  * the partials gathered before one merge; the merge is associative -- see

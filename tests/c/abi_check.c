@@ -116,6 +116,29 @@ int main(void) {
                                     NULL, 0, 0, NULL, 0, 0, 0, 32, 8, 128, 64, 0, 0, 0.088f, NULL,
                                     0, 0, NULL, 0, NULL),
          GQA_OK);
+  {
+    int32_t* T = (int32_t*)P;
+    expect("fused NULL tickets",
+           gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,
+                                              0.088f, NULL, 1024, P, 1 << 30, NULL, 512, NULL),
+           GQA_ERR_INVALID_ARGUMENT);
+    expect("fused 511 tickets",
+           gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,
+                                              0.088f, NULL, 1024, P, 1 << 30, T, 511, NULL),
+           GQA_ERR_WORKSPACE);
+    expect("fused group 64",
+           gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 64, 1, 8192, 128, NULL,
+                                              0.088f, NULL, 1024, P, 1 << 30, T, 1024, NULL),
+           GQA_ERR_UNSUPPORTED);
+    expect("fused tile 0",
+           gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,
+                                              0.088f, NULL, 0, P, 1 << 30, T, 512, NULL),
+           GQA_ERR_INVALID_ARGUMENT);
+    expect("fused small workspace",
+           gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,
+                                              0.088f, NULL, 1024, P, 1024, T, 512, NULL),
+           GQA_ERR_WORKSPACE);
+  }
   printf("%s\n", failures ? "FAILED" : "ALL OK");
   return failures ? 1 : 0;
 }

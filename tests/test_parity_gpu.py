@@ -319,6 +319,55 @@ def test_decode_head_dims(d, tile):
     assert_close(got, oracle_dense(inp), f"decode d={d} tile={tile}")
 
 
+# in-kernel split merge (one launch): B, Hq, Hkv, Skv, d
+FUSED_CASES = [
+    (4, 32, 8, 3000, 128),   # G = 4, one 16-column block
+    (3, 32, 1, 2500, 128),   # G = 32, two blocks
+    (2, 16, 4, 5000, 64),
+    (2, 8, 4, 1800, 256),    # d = 256 (one block per q-tile)
+    (2, 8, 8, 900, 32),      # G = 1
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+@pytest.mark.parametrize("tile", [1024, 64])
+def test_decode_fused(case, tile):
+    B, Hq, Hkv, Skv, d = FUSED_CASES[case]
+    note(f"fused decode {FUSED_CASES[case]} tile={tile}")
+    inp = workloads.make_dense(B, Hq, Hkv, 1, Skv, d, seed=60 + case, kv_len="random", sink=True,
+                               nan_pad=True)
+    g = to_dev(inp)
+    tickets = torch.zeros(B * Hq, dtype=torch.int32, device=dev())
+    kw = dict(kv_len=g["kv_len"], scale=inp["scale"], sink=g["sink"], tile_s_kv=tile)
+    outs = []
+    for _ in range(3):  # the tickets must come back to zero after every call
+        outs.append(gqa().decode_splitkv(g["q"], g["k"], g["v"], fused=True, tickets=tickets,
+                                         **kw))
+        torch.cuda.synchronize()
+        assert int(tickets.abs().sum()) == 0
+    got = outs[0].float().cpu().numpy()
+    assert_close(got, oracle_dense(inp), f"fused decode case={case} tile={tile}")
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    two = gqa().decode_splitkv(g["q"], g["k"], g["v"], **kw).float().cpu().numpy()
+    assert np.abs(got - two).max() <= 2 * 2.0 ** -8 * np.abs(two).max() + 1e-6
+
+
+def test_decode_fused_full_size():
+    c = workloads.CASES["decode_splitkv"]
+    note(f"fused decode full size {c}")
+    inp = workloads.make_case(c)
+    g = to_dev(inp)
+    tickets = torch.zeros(c.B * c.Hq, dtype=torch.int32, device=dev())
+    out = gqa().decode_splitkv(g["q"], g["k"], g["v"], kv_len=g["kv_len"], scale=inp["scale"],
+                               tile_s_kv=c.tile_s_kv, fused=True, tickets=tickets)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    assert np.all(np.isfinite(out)) and int(tickets.abs().sum()) == 0
+    got, want = _sampled_rows(inp, out, _rows(c, 160, 7), False)
+    assert_close(got, want, "fused decode full size")
+
+
 @pytest.mark.parametrize("d", [32, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_paged_head_dims(d, causal):

@@ -57,7 +57,10 @@
  * Ownership: the caller owns all memory and keeps it alive until the work
  * enqueued on `stream` completes.  The library never allocates, frees,
  * synchronises or reads device memory from the host, keeps no pointer after
- * returning, and is reentrant.  Launches are asynchronous.
+ * returning, and is reentrant.  Launches are asynchronous and are the only
+ * stream operations (no memset or copy), so every entry point can be
+ * captured into a HIP graph; a kernel's first launch in the process sets its
+ * LDS limit, so call each form once before capturing it.
  *
  * Errors: every function returns a gqa_status_t.  All validation happens
  * before anything is enqueued: on any status other than GQA_OK or

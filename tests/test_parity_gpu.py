@@ -499,3 +499,71 @@ def test_empty_batch_is_noop():
     k = torch.empty(0, 1, 5, 64, dtype=torch.bfloat16, device=D)
     out = gqa().prefill(q, k, k)
     assert out.shape == q.shape
+
+
+# ---------------------------------------------------------------- graph capture
+
+def _graph_cases():
+    """(name, fn(out) -> None, out) for every entry point, inputs on the GPU."""
+    m = gqa()
+    cases = []
+    inp = workloads.make_dense(2, 32, 8, 1, 3000, 128, seed=91, kv_len="random", sink=True)
+    g = to_dev(inp)
+    kw = dict(kv_len=g["kv_len"], scale=inp["scale"], sink=g["sink"])
+    ws = torch.empty(m.workspace_size(2, 32, 1, 3000, 128, 1024), dtype=torch.uint8, device=dev())
+    tk = torch.zeros(64, dtype=torch.int32, device=dev())
+    cases.append(("decode split", lambda o: m.decode_splitkv(g["q"], g["k"], g["v"], tile_s_kv=1024,
+                                                            out=o, workspace=ws, **kw), g["q"]))
+    cases.append(("decode fused", lambda o: m.decode_splitkv(g["q"], g["k"], g["v"], tile_s_kv=1024,
+                                                            out=o, workspace=ws, fused=True,
+                                                            tickets=tk, **kw), g["q"]))
+    inp2 = workloads.make_dense(1, 16, 4, 100, 700, 64, seed=92, kv_len="random", sink=True)
+    g2 = to_dev(inp2)
+    kw2 = dict(kv_len=g2["kv_len"], scale=inp2["scale"], sink=g2["sink"], causal=True)
+    ws2 = torch.empty(m.workspace_size(1, 16, 100, 700, 64, 256), dtype=torch.uint8, device=dev())
+    cases.append(("prefill one pass", lambda o: m.prefill(g2["q"], g2["k"], g2["v"], out=o, **kw2),
+                  g2["q"]))
+    cases.append(("prefill split", lambda o: m.prefill(g2["q"], g2["k"], g2["v"], tile_s_kv=256,
+                                                      out=o, workspace=ws2, **kw2), g2["q"]))
+    w = workloads.make_paged(B=3, Hq=16, Hkv=4, d=128, q_lens=[1, 5, 2], kv_lens=[300, 90, 1000],
+                             seed=93)
+    kn, vn, kh, vh = workloads.take_new_kv(w)
+    gw = to_dev(w)
+    kc, vc, kn, vn = kh.to(dev()), vh.to(dev()), kn.to(dev()), vn.to(dev())
+    pk = dict(max_q_len=w["max_q_len"], scale=w["scale"], sink=gw["sink"])
+    cases.append(("paged", lambda o: m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"],
+                                             gw["v_cache"], gw["page_table"], gw["kv_len"], out=o,
+                                             **pk), gw["q"]))
+    cases.append(("paged append", lambda o: m.paged_append(gw["q"], gw["cu_seqlens_q"], kc, vc,
+                                                           gw["page_table"], gw["kv_len"], kn, vn,
+                                                           out=o, **pk), gw["q"]))
+    return cases
+
+
+def test_graph_replay_matches_eager():
+    """Each entry point captured in a HIP graph replays bit-identically to its
+    eager call, three times, with eager launches and a synchronisation between
+    the replays (and the output cleared before each)."""
+    note("graph capture of every entry point")
+    for name, fn, like in _graph_cases():
+        eager = torch.empty_like(like)
+        fn(eager)
+        torch.cuda.synchronize()
+        out = torch.empty_like(like)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(out)  # first use on this stream outside the capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            fn(out)
+        for r in range(3):
+            out.zero_()
+            graph.replay()
+            other = torch.empty_like(like)
+            fn(other)  # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"{name} replay {r}"
+            assert torch.equal(other.view(torch.int16), eager.view(torch.int16)), name

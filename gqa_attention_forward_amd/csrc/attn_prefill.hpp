@@ -67,6 +67,8 @@ struct PrefillCfg {
 };
 
 constexpr float kLazyRescale = 8.f;  // log2 units
+// paged grids order their work by sequence length up to this many sequences
+constexpr int kRankedMaxB = 256;
 
 // Row maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950):
 // fmaxf would first quiet each input with an extra instruction.  The scores
@@ -85,6 +87,25 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The r-th sequence by decreasing kv_len (ties by index): a bijection of
+// 0 .. B-1, computed with one lane per sequence.  Wave-uniform result.
+__device__ __forceinline__ int seq_by_rank(const int32_t* kv_len, int B, int r, int lane) {
+  const __attribute__((address_space(4))) int32_t* kl =
+      (const __attribute__((address_space(4))) int32_t*)kv_len;
+  for (int base = 0; base < B; base += 64) {
+    const int l = base + lane;
+    const int wl = l < B ? kv_len[l] : 0;
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int wj = kl[j];  // uniform: a scalar load
+      rank += (wj > wl) || (wj == wl && j < l);
+    }
+    const uint64_t hit = __ballot(l < B && rank == r);
+    if (hit) return base + (int)__builtin_ctzll(hit);
+  }
+  return r;  // not reached: ranks are a permutation of 0 .. B-1
 }
 
 template <int D, int NW, bool PAGED, bool PARTIAL>
@@ -106,13 +127,26 @@ attn_prefill_kernel(const AttnArgs a) {
   const int hl = lane >> 5;
 
   const int L = blockIdx.x;
-  const int nbg = a.B * a.Hkv;
-  const int bg = L % nbg;
-  const int rest = L / nbg;
-  const int split = rest % a.n_split;
-  const int qt = a.n_qtiles - 1 - rest / a.n_split;  // late (heavy causal) q-tiles first
-  const int b = bg / a.Hkv;
-  const int g = bg % a.Hkv;
+  int b, g, split, qt;
+  if (PAGED && a.B <= kRankedMaxB) {
+    // Ragged sequences: the longest first, all of a sequence's work units
+    // together (late q-tiles first), so the heaviest workgroups start in the
+    // first wave of the grid and the light ones fill in behind them.
+    const int per_seq = a.Hkv * a.n_split * a.n_qtiles;
+    const int rem = L % per_seq;
+    b = seq_by_rank(a.kv_len, a.B, L / per_seq, lane);
+    g = rem % a.Hkv;
+    split = (rem / a.Hkv) % a.n_split;
+    qt = a.n_qtiles - 1 - rem / (a.Hkv * a.n_split);
+  } else {
+    const int nbg = a.B * a.Hkv;
+    const int bg = L % nbg;
+    const int rest = L / nbg;
+    split = rest % a.n_split;
+    qt = a.n_qtiles - 1 - rest / a.n_split;  // late (heavy causal) q-tiles first
+    b = bg / a.Hkv;
+    g = bg % a.Hkv;
+  }
   const int G = a.G;
 
   int q_len, q_row0 = 0;

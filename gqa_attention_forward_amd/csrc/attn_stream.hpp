@@ -13,10 +13,16 @@
 // runs per workgroup stream HBM faster than one split each (fewer, longer
 // sequential streams), while the partials keep the split size.
 //
+// Two options ride on the same kernel: the paged append (the query tokens'
+// own K/V come from k_new / v_new and are written into their pages; block
+// after the key loop) and the in-kernel split merge (tickets; block after
+// the partial write-out).
+//
 // MFMA mapping, v_mfma_f32_16x16x32_bf16 (16 query columns per block, so a
 // 4-row GQA group wastes 12 columns instead of 28 with the 32-wide form):
 //   S^T[key][q] = K Q^T : A = K straight from global memory (lane = key row
-//                         c16, 8 d per lane group), B = Q in registers.
+//                         c16, 8 d per lane group), B = Q in registers (in
+//                         LDS at d = 256).
 //   O^T[d][q] += V^T P^T: B = P from the S^T accumulators of the lane (two
 //                         16-key blocks -> 8 keys), A = V^T read from a
 //                         wave-private row-major LDS tile with

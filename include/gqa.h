@@ -88,7 +88,7 @@ typedef int32_t gqa_status_t;
 #define GQA_ERR_INVALID_ARGUMENT 1 /* NULL required pointer, bad dims, Hq % Hkv != 0, bad flag */
 #define GQA_ERR_UNSUPPORTED 2      /* d not 32/64/128/256, misaligned pointer or stride,
                                       page_size != 64, a group beyond the append/fused limits */
-#define GQA_ERR_WORKSPACE 3        /* workspace (or tickets) NULL or too small */
+#define GQA_ERR_WORKSPACE 3        /* workspace NULL or too small; ticket array too small */
 #define GQA_ERR_HIP 4              /* a HIP launch failed; message from hipGetErrorString */
 
 /* GQA_ABI_VERSION of the built library. */

@@ -230,6 +230,11 @@ def test_paged_append_decode_full_size():
     assert_close(out[t, h], want, "paged append decode full size")
     assert torch.equal(kc.cpu().view(torch.int16), w["k_cache"].view(torch.int16))
     assert torch.equal(vc.cpu().view(torch.int16), w["v_cache"].view(torch.int16))
+    # the plain paged decode over the (now complete) cache, as the bench times it
+    plain = gqa().paged(g["q"], g["cu_seqlens_q"], kc, vc, g["page_table"], g["kv_len"],
+                        max_q_len=1, scale=w["scale"], tile_s_kv=1024)
+    torch.cuda.synchronize()
+    assert_close(plain.float().cpu().numpy()[t, h], want, "paged decode full size")
 
 
 @pytest.mark.parametrize("G", [4, 32])

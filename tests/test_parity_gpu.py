@@ -237,6 +237,23 @@ def test_paged_append_decode_full_size():
     assert_close(plain.float().cpu().numpy()[t, h], want, "paged decode full size")
 
 
+@pytest.mark.parametrize("tile", [0, 256])
+def test_paged_head_major_pages(tile):
+    """Pools stored head-major ([page][kv head][row][d]) and passed by strides
+    give the same result as the oracle over the logical [page][row][h][d] view."""
+    note(f"paged head-major pages tile={tile}")
+    w = workloads.make_paged(B=4, Hq=16, Hkv=4, d=128, q_lens=[1, 9, 3, 30],
+                             kv_lens=[500, 64, 1300, 90], seed=35)
+    g = to_dev(w)
+    kc = g["k_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vc = g["v_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert kc.stride(1) == 128 and kc.stride(2) == 64 * 128
+    out = gqa().paged(g["q"], g["cu_seqlens_q"], kc, vc, g["page_table"], g["kv_len"],
+                      max_q_len=w["max_q_len"], scale=w["scale"], sink=g["sink"], tile_s_kv=tile)
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().numpy(), _paged_oracle(w), f"head-major pages tile={tile}")
+
+
 @pytest.mark.parametrize("G", [4, 32])
 @pytest.mark.parametrize("tile", [0, 1024])
 def test_paged_decode_shape(G, tile):

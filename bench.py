@@ -1,6 +1,6 @@
 """Benchmark of the GQA forward hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--only NAME]
 
 A step is one call of the hot path over one batch of synthetic input, with
 inputs already resident in HBM.  The default workload is the split-KV decode
@@ -15,8 +15,12 @@ kernel); `value` is its K/V-stream throughput in GB/s of algorithmic bytes
   (profiles/decode_partial_hbm_traffic.txt), null once the kernel sources
   differ from the ones it was measured on;
 * secondary: the other named workloads (short-q/long-kv prefill, causal
-  prefill, ragged paged, tiny prefill), each timed the same way with its own
-  roofline fraction;
+  prefill, ragged paged, causal chunked prefill, the other head dims, paged
+  decode with and without the fused append, the in-kernel merge, tiny
+  prefill), each timed the same way with its own roofline fraction;
+* cold_cache: the decode, short-q and causal workloads again, one call per
+  HIP-event pair with a 512 MiB buffer read before each (outside the events)
+  so the L2 caches and the MALL start cold; median and min;
 * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
   sample of the decode workload.
 
@@ -133,6 +137,36 @@ def time_graph(fn, reps, replays, stream):
     return start.elapsed_time(stop) / (reps * replays)
 
 
+def time_cold(fn, stream, flush, min_iters=50, min_ms=200.0):
+    """(median, min) ms of single calls of `fn`, each timed with its own HIP
+    events after all of `flush` (>= 512 MiB) is read, outside the events, so
+    that the L2 caches and the 256 MB MALL hold none of the inputs.  The
+    flush reads rather than writes: rewritten lines would sit dirty in the
+    caches and be written back during the timed call (+55% on the decode).
+    At least `min_iters` calls or `min_ms` of timed work, whichever is more."""
+    words = flush.view(torch.int32)
+    total = torch.empty((), dtype=torch.int64, device=flush.device)
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            torch.sum(words, dim=(0,), dtype=torch.int64, out=total)
+            fn()
+        torch.cuda.synchronize()
+        per = time_loop(fn, 3, 0, stream)
+        iters = int(max(min_iters, min_ms / max(per, 1e-3)))
+        marks = []
+        for _ in range(iters):
+            torch.sum(words, dim=(0,), dtype=torch.int64, out=total)
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            fn()
+            stop.record(stream)
+            marks.append((start, stop))
+        torch.cuda.synchronize()
+    times = sorted(a.elapsed_time(b) for a, b in marks)
+    return times[len(times) // 2], times[0], iters
+
+
 # Kernel sources behind the split-KV partial kernel; the committed counter
 # summary records their hash.
 PARTIAL_SOURCES = ("attn_stream.hpp", "common.hpp", "gqa_api.hip")
@@ -226,6 +260,39 @@ def bench_decode(args, device, stream):
         "kernel_ms": {"partial": round(ms_p, 5), "merge": round(ms_m, 5)},
         "kernel_bytes_per_launch": {"partial": read_bytes},
     }
+
+
+def bench_cold(device, stream):
+    """The decode, short-q and causal workloads with cold caches before every
+    call: median and min over single timed calls."""
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=device)
+    res = {}
+    c, _, g = setup_dense("decode_splitkv", device)
+    step, _, _, _ = decode_step_fns(g, c)
+    med, mn, it = time_cold(step, stream, flush)
+    tb, _ = dense_bytes(c)
+    res["decode_splitkv"] = {"median_ms": round(med, 5), "min_ms": round(mn, 5), "calls": it,
+                             "GB/s": round(tb / (med * 1e-3) / 1e9, 1),
+                             "roofline_frac": round(tb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del g
+    c, _, g = setup_dense("shortq_longkv", device)
+    step, _ = prefill_step_fn(g, c, 2048)
+    med, mn, it = time_cold(step, stream, flush)
+    tb, _ = dense_bytes(c)
+    res["shortq_longkv_tile2048"] = {"median_ms": round(med, 5), "min_ms": round(mn, 5),
+                                     "calls": it, "GB/s": round(tb / (med * 1e-3) / 1e9, 1),
+                                     "roofline_frac": round(tb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del g
+    c, _, g = setup_dense("causal_prefill", device)
+    step, _ = prefill_step_fn(g, c, 0)
+    warm_steps(step, stream)  # let the clock ramp first
+    med, mn, it = time_cold(step, stream, flush)
+    fl = dense_flops(c)
+    res["causal_prefill"] = {"median_ms": round(med, 5), "min_ms": round(mn, 5), "calls": it,
+                             "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 2),
+                             "roofline_frac": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del g, flush
+    return res
 
 
 def bench_secondary(args, device, stream):
@@ -472,6 +539,7 @@ def main():
 
     c, inp, dec = bench_decode(args, device, stream)
     secondary = None if args.no_secondary else bench_secondary(args, device, stream)
+    cold = None if args.no_secondary else bench_cold(device, stream)
     cpu = cpu_baseline(inp, c, args.cpu_budget) if args.cpu_budget > 0 else None
 
     line = {
@@ -495,6 +563,7 @@ def main():
         "kernel_bytes_per_launch": dec["kernel_bytes_per_launch"],
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "cold_cache": cold,
     }
     print(json.dumps(line), flush=True)
 

@@ -589,3 +589,47 @@ def test_graph_replay_matches_eager():
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"{name} replay {r}"
             assert torch.equal(other.view(torch.int16), eager.view(torch.int16)), name
+
+
+# ---------------------------------------------------------------- long contexts
+
+def test_long_context_128k():
+    """131072 keys: split-KV decode (128 splits, runs of splits), the in-kernel
+    merge, a one-pass 16-query prefill over the same keys, and a paged decode
+    over ~1600 pages; sampled rows against the oracle."""
+    note("long context: 131072 keys")
+    inp = workloads.make_dense(2, 16, 2, 1, 131072, 128, seed=77, kv_len=[131072, 100003],
+                               sink=True, nan_pad=True)
+    g = to_dev(inp)
+    kw = dict(kv_len=g["kv_len"], scale=inp["scale"], sink=g["sink"])
+    m = gqa()
+    rows = (np.repeat([0, 1], 8), np.tile(np.arange(0, 16, 2), 2), np.zeros(16, dtype=int))
+    k32, v32 = inp["k"].float().numpy(), inp["v"].float().numpy()
+    want = oracle.attention_rows_fp64(inp["q"].float().numpy(), k32, v32, *rows, scale=inp["scale"],
+                                      kv_len=inp["kv_len"].numpy(), sink=to_f64(inp["sink"]))
+    for label, out in (("split", m.decode_splitkv(g["q"], g["k"], g["v"], tile_s_kv=1024, **kw)),
+                       ("fused", m.decode_splitkv(g["q"], g["k"], g["v"], tile_s_kv=1024,
+                                                  fused=True, **kw))):
+        torch.cuda.synchronize()
+        assert_close(out.float().cpu().numpy()[rows], want, f"128k decode {label}")
+    # 16 queries at the end of the same keys (bottom-right causal), one pass
+    q16 = workloads.make_dense(2, 16, 2, 16, 8, 128, seed=78)["q"]
+    out = m.prefill(q16.to(dev()), g["k"], g["v"], causal=True, **kw)
+    torch.cuda.synchronize()
+    r16 = (np.repeat([0, 1], 8), np.tile(np.arange(0, 16, 2), 2), np.tile([0, 15, 7, 3], 4))
+    want16 = oracle.attention_rows_fp64(q16.float().numpy(), k32, v32, *r16, scale=inp["scale"],
+                                        kv_len=inp["kv_len"].numpy(), sink=to_f64(inp["sink"]),
+                                        causal=True)
+    assert_close(out.float().cpu().numpy()[r16], want16, "128k prefill")
+    # paged decode over the same lengths
+    w = workloads.make_paged(B=2, Hq=16, Hkv=2, d=128, q_lens=[1, 1], kv_lens=[100000, 3000],
+                             seed=79)
+    outp = _paged_run(w, tile=1024)
+    t = np.repeat([0, 1], 8)
+    h = np.tile(np.arange(0, 16, 2), 2)
+    wp = oracle.paged_attention_rows_fp64(w["q"].float().numpy(), w["cu_seqlens_q"].numpy(),
+                                          w["k_cache"].float().numpy(),
+                                          w["v_cache"].float().numpy(), w["page_table"].numpy(),
+                                          w["kv_len"].numpy(), t, h, scale=w["scale"],
+                                          page_size=64, sink=to_f64(w["sink"]))
+    assert_close(outp[t, h], wp, "100k paged decode")

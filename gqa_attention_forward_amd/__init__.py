@@ -15,6 +15,7 @@ eager fallback: without the built library every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 
 import torch
@@ -52,8 +53,14 @@ def _bhsd(name, t):
         raise ValueError(f"{name} must have a contiguous head dim")
 
 
+@functools.lru_cache(maxsize=None)
+def _default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to fp32 (the value the kernels and the oracle use)."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
 def _scale(scale, d):
-    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32)) if scale is None else float(scale)
+    return _default_scale(int(d)) if scale is None else float(scale)
 
 
 def n_splits(Skv: int, tile_s_kv: int) -> int:
@@ -61,6 +68,8 @@ def n_splits(Skv: int, tile_s_kv: int) -> int:
 
 
 def workspace_size(B, Hq, Sq, Skv, d, tile_s_kv) -> int:
+    if tile_s_kv == 0:
+        return 0  # one pass needs no workspace (the library reports 0 too)
     out = ctypes.c_size_t(0)
     _lib.check(_lib.load().gqa_attention_workspace_size(B, Hq, Sq, Skv, d, tile_s_kv,
                                                         ctypes.byref(out)))

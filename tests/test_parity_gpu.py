@@ -401,17 +401,19 @@ def test_paged_head_dims(d, causal):
     assert_close(_paged_run(w, causal=causal, tile=128), want, f"paged d={d} c={causal} split")
 
 
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 32])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 32, 64])
 def test_group_sizes(G):
-    """The pages' SDPA-checked group sizes (AstrAI commit log, HB packing commit)."""
+    """The pages' SDPA-checked group sizes (AstrAI commit log, HB packing commit),
+    and G = 64, whose single-token rows already take the shared-tile kernel."""
     Hkv = 2 if G <= 8 else 1
     note(f"group size G={G}")
     for Sq in (1, 9, 64):
         inp = workloads.make_dense(2, Hkv * G, Hkv, Sq, 200, 128, seed=50 + G + Sq,
                                    kv_len="random", sink=G % 2 == 0, nan_pad=True)
-        got = run_dense(inp, causal=Sq > 1)
         want = oracle_dense(inp, causal=Sq > 1)
-        assert_close(got, want, f"G={G} Sq={Sq}")
+        for tile in (0, 64):
+            got = run_dense(inp, causal=Sq > 1, tile=tile)
+            assert_close(got, want, f"G={G} Sq={Sq} tile={tile}")
 
 
 @pytest.mark.parametrize("Skv", [1, 63, 1024, 3000])

@@ -447,13 +447,14 @@ def run_only(args, device, stream):
         _, partial, _, _ = decode_step_fns(g, c)
         ms = time_loop(partial, args.steps, args.warmup, stream)
         return {"workload": name, "ms": ms, "GB/s": dense_bytes(c)[1] / (ms * 1e-3) / 1e9}
-    if name == "ragged_paged":
+    if name in ("ragged_paged", "ragged_paged_onepass"):
         w = workloads.make_paged()
         gw = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
         m = gqa()
+        tile = 1024 if name == "ragged_paged" else 0
         fn = lambda: m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],  # noqa: E731
                              gw["page_table"], gw["kv_len"], max_q_len=w["max_q_len"],
-                             scale=w["scale"], sink=gw["sink"], tile_s_kv=1024)
+                             scale=w["scale"], sink=gw["sink"], tile_s_kv=tile)
         return {"workload": name, "ms": time_loop(fn, args.steps, args.warmup, stream)}
     if name == "paged_decode_append":
         w = workloads.make_paged_decode()
@@ -521,7 +522,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--only", choices=["decode_partial", "shortq_longkv", "causal_prefill",
-                                       "ragged_paged", "paged_causal_chunked",
+                                       "ragged_paged", "ragged_paged_onepass",
+                                       "paged_causal_chunked",
                                        "paged_decode_append", "copy"],
                     help="profiling aid: time only this workload's kernels and print its line")
     args = ap.parse_args()

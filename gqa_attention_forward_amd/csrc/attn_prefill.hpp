@@ -48,22 +48,35 @@
 
 namespace gqa {
 
-template <int D, int NW>
+// KS = 2 splits the workgroup's key range between two groups of NW / 2
+// waves over the same rows (alternate tiles, each group with its own pair of
+// LDS stages); the groups combine their (m, l, O) in LDS at the end.  It
+// halves the longest key walk of a workgroup where the grid is too small for
+// the load to even out across CUs.
+template <int D, int NW, int KS = 1>
 struct PrefillCfg {
+  static_assert(KS == 1 || KS == 2, "key groups per workgroup");
   static constexpr int BK = 64;              // keys per tile
   static constexpr int DC = D / 8;           // 16-byte chunks per row
   static constexpr int NT = NW * 64;
-  static constexpr int ROWS = 32 * NW;       // query rows per workgroup
+  static constexpr int NWH = NW / KS;        // waves per key group
+  static constexpr int NTH = NWH * 64;       // threads per key group (they stage its tiles)
+  static constexpr int ROWS = 32 * NWH;      // query rows per workgroup
   static constexpr int KP = D + 8;           // K row pitch (elements): padded, not swizzled
   static constexpr int KTILE = BK * KP;      // elements of one K tile
   static constexpr int TILE = BK * D;        // elements of one V tile
   static constexpr int STAGE = KTILE + TILE; // K then V
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  // workgroups per CU that fit in 160 KiB of LDS (one at d = 256)
+  static constexpr int LDS_BYTES = KS * 2 * STAGE * 2;
+  // the launch bound's minimum waves per SIMD: 2 where two sets of stages
+  // fit in 160 KiB of LDS, else 1 (d = 256, or two key groups at d = 128).
+  // An 8-wave workgroup is 2 waves per SIMD either way (one per CU).
   static constexpr int WG_PER_CU = 2 * LDS_BYTES <= 160 * 1024 ? 2 : 1;
-  static constexpr int CPT = BK * DC / NT;   // chunks per thread per tensor
-  static_assert(CPT >= 1 && BK * DC % NT == 0 && NT % DC == 0, "tile split");
-  static_assert((NT / DC) % 8 == 0, "chunk rows keep the V swizzle");
+  static constexpr int CPT = BK * DC / NTH;  // chunks per thread per tensor
+  static_assert(CPT >= 1 && BK * DC % NTH == 0 && NTH % DC == 0, "tile split");
+  static_assert((NTH / DC) % 8 == 0, "chunk rows keep the V swizzle");
+  // the combine parks one group's accumulators (D / 2 floats per lane), m,
+  // m_true and l
+  static_assert(KS == 1 || NWH * 64 * (D / 2 + 4) * 4 <= LDS_BYTES, "combine fits the stages");
 };
 
 constexpr float kLazyRescale = 8.f;  // log2 units
@@ -108,11 +121,11 @@ __device__ __forceinline__ int seq_by_rank(const int32_t* kv_len, int B, int r, 
   return r;  // not reached: ranks are a permutation of 0 .. B-1
 }
 
-template <int D, int NW, bool PAGED, bool PARTIAL>
-__global__ void __launch_bounds__(NW * 64, (PrefillCfg<D, NW>::WG_PER_CU))
+template <int D, int NW, bool PAGED, bool PARTIAL, int KS = 1>
+__global__ void __launch_bounds__(NW * 64, (PrefillCfg<D, NW, KS>::WG_PER_CU))
 attn_prefill_kernel(const AttnArgs a) {
-  using C = PrefillCfg<D, NW>;
-  constexpr int NT = C::NT;
+  using C = PrefillCfg<D, NW, KS>;
+  constexpr int NTH = C::NTH;
   constexpr int BK = C::BK;
   constexpr int DC = C::DC;
   constexpr int CPT = C::CPT;
@@ -123,6 +136,8 @@ attn_prefill_kernel(const AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int kh = KS == 1 ? 0 : wv / C::NWH;                  // key group
+  const int wq = KS == 1 ? wv : wv % C::NWH;                 // 32-row block
   const int col = lane & 31;
   const int hl = lane >> 5;
 
@@ -172,14 +187,20 @@ attn_prefill_kernel(const AttnArgs a) {
     kend = min(kend, min(max(n - q_len + p_last + 1, 0), n));
   }
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  // this key group's tiles are kh, kh + KS, ...; every group runs nsteps
+  // steps (one barrier each), idling through the ones it has no tile for
+  const int ntl = ntiles > kh ? (ntiles - kh + KS - 1) / KS : 0;
+  const int nsteps = (ntiles + KS - 1) / KS;
 
   // ---- this lane's query row and masking bounds
-  const int wrow0 = row0 + 32 * wv;
+  const int wrow0 = row0 + 32 * wq;
   int wlo = kend;  // below wlo no row of the wave is masked
   if (a.causal) wlo = min(kend, min(max(n - q_len + wrow0 / G + 1, 0), n));
   if (wrow0 >= rows_total) wlo = kbeg;
-  // tiles [0, nfull) need no mask for any row of this wave
-  const int nfull = min(ntiles, max(0, (wlo - kbeg) / BK));
+  // tiles [0, nfull_all) need no mask for any row of this wave; nfull of
+  // them are this group's
+  const int nfull_all = min(ntiles, max(0, (wlo - kbeg) / BK));
+  const int nfull = nfull_all > kh ? (nfull_all - kh + KS - 1) / KS : 0;
   const int rho = wrow0 + col;
   const bool rvalid = rho < rows_total;
   const int pq = rvalid ? rho / G : 0;
@@ -210,20 +231,22 @@ attn_prefill_kernel(const AttnArgs a) {
   // ---- K/V staging.  A 64-key tile is one page of the paged layout; it is
   // loaded through one buffer resource per tensor that starts at the tile
   // and ends at its last row before kv_len, so rows past kv_len read as
-  // zeros without touching memory (and are masked).  Chunk i of a thread is
-  // row tid / DC + i NT / DC at a per-thread constant offset.
+  // zeros without touching memory (and are masked).  The threads of a key
+  // group stage its tiles: chunk i of group thread t is row t / DC +
+  // i NTH / DC at a per-thread constant offset.
   struct Stage {
     u32x4 k[CPT];
     u32x4 v[CPT];
   };
   const uint32_t kss2 = (uint32_t)(PAGED ? a.kv_sr : a.k_ss) * 2u;
   const uint32_t vss2 = (uint32_t)(PAGED ? a.kv_sr : a.v_ss) * 2u;
-  const int srow = tid / DC, sch = tid % DC;
+  const int gt = KS == 1 ? tid : tid % NTH;  // thread within the key group
+  const int srow = gt / DC, sch = gt % DC;
   uint32_t koff[CPT], voff[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    koff[i] = (uint32_t)(srow + i * (NT / DC)) * kss2 + 16u * sch;
-    voff[i] = (uint32_t)(srow + i * (NT / DC)) * vss2 + 16u * sch;
+    koff[i] = (uint32_t)(srow + i * (NTH / DC)) * kss2 + 16u * sch;
+    voff[i] = (uint32_t)(srow + i * (NTH / DC)) * vss2 + 16u * sch;
   }
   const uint16_t* khead = a.k + (PAGED ? (int64_t)g * a.k_sh
                                        : (int64_t)b * a.k_sb + (int64_t)g * a.k_sh);
@@ -250,19 +273,22 @@ attn_prefill_kernel(const AttnArgs a) {
   // the rows of a thread's chunks differ by multiples of 8: one swizzle
   const int kst = srow * C::KP + 8 * sch;
   const int vst = srow * D + 8 * (sch ^ vslot_swz<DC>(srow));
+  uint16_t* const sg = smem + kh * 2 * C::STAGE;  // this group's two stages
   auto store_tile = [&](int stage, const Stage& st) {
-    uint16_t* Ks = smem + stage * C::STAGE;
+    uint16_t* Ks = sg + stage * C::STAGE;
     uint16_t* Vs = Ks + C::KTILE;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      *reinterpret_cast<u32x4*>(Ks + kst + i * (NT / DC) * C::KP) = st.k[i];
-      *reinterpret_cast<u32x4*>(Vs + vst + i * (NT / DC) * D) = st.v[i];
+      *reinterpret_cast<u32x4*>(Ks + kst + i * (NTH / DC) * C::KP) = st.k[i];
+      *reinterpret_cast<u32x4*>(Vs + vst + i * (NTH / DC) * D) = st.v[i];
     }
   };
+  // first key of this group's it-th tile
+  auto tile_key = [&](int it) { return kbeg + (it * KS + kh) * BK; };
 
   Stage nx;
-  if (ntiles > 0) {
-    load_tile(kbeg, nx);
+  if (ntl > 0) {
+    load_tile(tile_key(0), nx);
     store_tile(0, nx);
   }
   lds_barrier();
@@ -394,8 +420,9 @@ attn_prefill_kernel(const AttnArgs a) {
   // Whole-phase operand fetches (EARLY): each phase's LDS operands are
   // requested before the previous phase's MFMAs, so none of its MFMAs waits
   // on LDS latency.  Needs 2 x D / 4 more VGPRs; only the 8-wave form at
-  // d <= 128 has them.
-  constexpr bool EARLY = (NW == 8 && D <= 128);
+  // d <= 128 has them, and with two key groups (twice the staging registers)
+  // only at d = 64: at d = 128 that form spills.
+  constexpr bool EARLY = (NW == 8 && D <= 128 && (KS == 1 || D <= 64));
   auto kfetch = [&](const uint16_t* Ks, int h, bf16x8 (&k)[NCK]) {
 #pragma unroll
     for (int c = 0; c < NCK; ++c) k[c] = kread(Ks, c, h);
@@ -443,9 +470,9 @@ attn_prefill_kernel(const AttnArgs a) {
   // address of the step is a base register plus an immediate
   auto step_early = [&](auto mask_tag, int it, auto par) {
     constexpr int PAR = decltype(par)::value;
-    const int j0 = kbeg + it * BK;
-    load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
-    const uint16_t* Ks = smem + PAR * C::STAGE;
+    const int j0 = tile_key(it);
+    load_tile(tile_key(min(it + 1, ntl - 1)), nx);
+    const uint16_t* Ks = sg + PAR * C::STAGE;
     const uint16_t* Vs = Ks + C::KTILE;
     bf16x8 k0[NCK], k1[NCK], v0[2 * NDB], v1[2 * NDB], p0[2], p1[2];
     kfetch(Ks, 0, k0);
@@ -475,11 +502,11 @@ attn_prefill_kernel(const AttnArgs a) {
     lds_barrier();
   };
   auto step = [&](auto mask_tag, int it) {
-    const int j0 = kbeg + it * BK;
+    const int j0 = tile_key(it);
     // Unconditional prefetch of the next tile (past the end it re-reads the
     // last tile, an L2 hit): no branch separates the loads from the compute.
-    load_tile(kbeg + min(it + 1, ntiles - 1) * BK, nx);
-    const uint16_t* Ks = smem + (it & 1) * C::STAGE;
+    load_tile(tile_key(min(it + 1, ntl - 1)), nx);
+    const uint16_t* Ks = sg + (it & 1) * C::STAGE;
     const uint16_t* Vs = Ks + C::KTILE;
     bf16x8 p0[2], p1[2];
     // 1. S_0
@@ -517,19 +544,59 @@ attn_prefill_kernel(const AttnArgs a) {
     if (it < nfull) {  // odd number of unmasked tiles
       step_early(False{}, it, P0{});
       ++it;
-      if (it < ntiles) {
+      if (it < ntl) {
         step_early(True{}, it, P1{});
         ++it;
       }
     }
-    for (; it + 1 < ntiles; it += 2) {
+    for (; it + 1 < ntl; it += 2) {
       step_early(True{}, it, P0{});
       step_early(True{}, it + 1, P1{});
     }
-    if (it < ntiles) step_early(True{}, it, P0{});
+    if (it < ntl) step_early(True{}, it, P0{});
   } else {
     for (; it < nfull; ++it) step(False{}, it);
-    for (; it < ntiles; ++it) step(True{}, it);
+    for (; it < ntl; ++it) step(True{}, it);
+  }
+  if constexpr (KS > 1) {
+    for (int i = ntl; i < nsteps; ++i) lds_barrier();  // steps this group has no tile for
+    // Combine the key groups (the same associative (m, l, O) merge as
+    // between splits): group 1 parks its O, reference, true max and sum
+    // share in the stages, which no wave reads after the last barrier;
+    // group 0 takes both to the larger reference.  Lane-major float4
+    // slots: the same lane of the same row block reads what it needs.
+    constexpr int XF = 64 * NDB * 16;  // accumulator floats of a row block
+    float* xo = reinterpret_cast<float*>(smem) + wq * XF;
+    float4* xm = reinterpret_cast<float4*>(reinterpret_cast<float*>(smem) + C::NWH * XF) + wq * 64;
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(xo + ((db * 4 + q4) * 64 + lane) * 4) =
+              make_float4(acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2],
+                          acc[db][4 * q4 + 3]);
+      xm[lane] = make_float4(mref, mtrue, l, 0.f);
+    }
+    lds_barrier();
+    if (kh == 1) return;
+    const float4 st1 = xm[lane];
+    const float mc = fmaxf(mref, st1.x);
+    const float f0 = mref == -INFINITY ? 0.f : ex2(mref - mc);
+    const float f1 = st1.x == -INFINITY ? 0.f : ex2(st1.x - mc);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 o1 = *reinterpret_cast<const float4*>(xo + ((db * 4 + q4) * 64 + lane) * 4);
+        acc[db][4 * q4] = acc[db][4 * q4] * f0 + o1.x * f1;
+        acc[db][4 * q4 + 1] = acc[db][4 * q4 + 1] * f0 + o1.y * f1;
+        acc[db][4 * q4 + 2] = acc[db][4 * q4 + 2] * f0 + o1.z * f1;
+        acc[db][4 * q4 + 3] = acc[db][4 * q4 + 3] * f0 + o1.w * f1;
+      }
+    l = l * f0 + st1.z * f1;
+    mref = mc;
+    mtrue = fmaxf(mtrue, st1.y);
   }
 
   // ---- epilogue; accumulator register j of d-block db holds

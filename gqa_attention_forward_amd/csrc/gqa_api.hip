@@ -8,6 +8,7 @@
 // synchronises or reads device memory from the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -125,11 +126,11 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
   return check_launch("attention kernel");
 }
 
-template <int D, int NW, bool PAGED, bool PARTIAL>
+template <int D, int NW, bool PAGED, bool PARTIAL, int KS = 1>
 gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  using C = gqa::PrefillCfg<D, NW>;
+  using C = gqa::PrefillCfg<D, NW, KS>;
   args.spw = 1;
-  return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL>, C::LDS_BYTES, C::NT,
+  return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS>, C::LDS_BYTES, C::NT,
                      args, rows, C::ROWS, stream);
 }
 
@@ -205,7 +206,29 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
   } else {
     if (rows <= 64) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
     if (D == 32 || rows <= 128) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
-    if constexpr (D != 32) return launch_prefill<D, 8, PAGED, PARTIAL>(args, rows, stream);
+    if constexpr (D != 32) {
+      // The 8-wave form holds one workgroup per CU.  A grid that fits the
+      // CUs in one round leaves no later workgroups to even out the load:
+      // its time is the longest key walk of a workgroup, which two key
+      // groups per workgroup halve.  Their grid is twice as large, and at
+      // 128 rows per tile a CU pulls twice the K/V bytes per flop, so they
+      // are taken only where that grid still fits one round, or where the
+      // walk is long (32 or more 64-key tiles: the longest one allowed by
+      // the split size or the key count).  Measured: ragged paged one pass
+      // (64 workgroups) 111 -> 70 us, with splits of 2048 72 -> 52 us, of
+      // 1024 (256 workgroups, 16 tiles) 48 us kept; causal 2048^2 at
+      // B = 1, Hkv = 8 (256 workgroups, 32 tiles) 62 -> 53 us; causal
+      // 4096^2 there (512 workgroups) 137 -> 160 us with two groups, kept.
+      using C1 = gqa::PrefillCfg<D, 8>;
+      const int64_t per = (int64_t)args.B * args.Hkv * args.n_split;
+      const int64_t n1 = per * cdiv(rows, C1::ROWS);
+      const int64_t n2 = per * cdiv(rows, gqa::PrefillCfg<D, 8, 2>::ROWS);
+      const int64_t keys = args.tile > 0 ? std::min<int64_t>(args.tile, args.Skv) : args.Skv;
+      const int64_t cus = device_cus();
+      if (n1 <= cus && (n2 <= cus || cdiv(keys, C1::BK) >= 32))
+        return launch_prefill<D, 8, PAGED, PARTIAL, 2>(args, rows, stream);
+      return launch_prefill<D, 8, PAGED, PARTIAL>(args, rows, stream);
+    }
   }
   return GQA_OK;  // not reached
 }

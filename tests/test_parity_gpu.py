@@ -416,6 +416,37 @@ def test_group_sizes(G):
             assert_close(got, want, f"G={G} Sq={Sq} tile={tile}")
 
 
+# The 8-wave prefill form splits a workgroup's keys between two wave groups
+# when its grid fits the 256 CUs in one round (at most 256 workgroups of 256
+# rows) and either the doubled grid still does or a workgroup may walk 32 or
+# more 64-key tiles; else it keeps one group.  These shapes sit on both sides
+# of the boundary (B, Hq, Hkv, S, d; workgroups = B Hkv ceil(S G / 256)),
+# with ragged last q-tiles, causal and not, one pass and split.
+KEY_GROUP_CASES = [
+    (1, 8, 2, 8192, 128),   # 256 workgroups: two key groups
+    (1, 8, 2, 8300, 128),   # 260: one group, ragged
+    (2, 16, 4, 2040, 64),   # 256: two key groups, ragged
+    (2, 16, 4, 2304, 64),   # 288: one group
+]
+
+
+@pytest.mark.parametrize("case", range(len(KEY_GROUP_CASES)))
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("tile", [0, 2048])
+def test_prefill_key_group_boundary(case, causal, tile):
+    B, Hq, Hkv, S, d = KEY_GROUP_CASES[case]
+    note(f"key-group boundary B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} causal={causal} tile={tile}")
+    inp = workloads.make_dense(B, Hq, Hkv, S, S, d, seed=70 + case, kv_len=[S - 5 * b for b in range(B)])
+    out = run_dense(inp, causal=causal, tile=tile, use_sink=False)
+    r = np.random.default_rng(case)
+    bi, hi, ii = r.integers(0, B, 96), r.integers(0, Hq, 96), r.integers(0, S, 96)
+    ii[:4] = [0, S - 1, S - 2, S // 2]
+    want = oracle.attention_rows_fp64(inp["q"].float().numpy(), inp["k"].float().numpy(),
+                                      inp["v"].float().numpy(), bi, hi, ii, scale=inp["scale"],
+                                      kv_len=inp["kv_len"].numpy(), causal=causal)
+    assert_close(out[bi, hi, ii], want, f"key groups case={case} causal={causal} tile={tile}")
+
+
 @pytest.mark.parametrize("Skv", [1, 63, 1024, 3000])
 def test_decode_sweep(Skv):
     note(f"decode Skv={Skv}")

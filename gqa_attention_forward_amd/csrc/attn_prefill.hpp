@@ -3,8 +3,11 @@
 // kv split); all NW waves share each 64-key K/V tile through LDS, so a tile
 // is fetched once per workgroup for every query head of the group (AstrAI
 // commit log, the commit that packs HB = min(G, warps) query heads per
-// block).  Each wave owns 32 query rows; two waves per SIMD (one workgroup
-// per CU at d = 256, whose double-buffered tiles take 130 KiB of LDS).
+// block).  Each wave owns 32 query rows.  The 8-wave form (d = 64, 128)
+// runs one workgroup per CU, two waves per SIMD with up to 256 VGPRs each;
+// d = 256 runs 4 waves, one per SIMD, its double-buffered tiles taking
+// 130 KiB of LDS.  The 8-wave form can also split a workgroup's keys between
+// two groups of 4 waves (KS = 2, PrefillCfg) where the grid is small.
 //
 // MFMA mapping, v_mfma_f32_32x32x16_bf16 (32 query rows are the N
 // dimension):
@@ -67,10 +70,11 @@ struct PrefillCfg {
   static constexpr int TILE = BK * D;        // elements of one V tile
   static constexpr int STAGE = KTILE + TILE; // K then V
   static constexpr int LDS_BYTES = KS * 2 * STAGE * 2;
-  // the launch bound's minimum waves per SIMD: 2 where two sets of stages
-  // fit in 160 KiB of LDS, else 1 (d = 256, or two key groups at d = 128).
-  // An 8-wave workgroup is 2 waves per SIMD either way (one per CU).
-  static constexpr int WG_PER_CU = 2 * LDS_BYTES <= 160 * 1024 ? 2 : 1;
+  // the launch bound's minimum waves per SIMD (it caps the registers a wave
+  // may take): 2 where two sets of stages fit in 160 KiB of LDS, else 1
+  // (d = 256, or two key groups at d = 128).  An 8-wave workgroup is 2 waves
+  // per SIMD either way, one workgroup per CU.
+  static constexpr int MIN_WAVES_PER_SIMD = 2 * LDS_BYTES <= 160 * 1024 ? 2 : 1;
   static constexpr int CPT = BK * DC / NTH;  // chunks per thread per tensor
   static_assert(CPT >= 1 && BK * DC % NTH == 0 && NTH % DC == 0, "tile split");
   static_assert((NTH / DC) % 8 == 0, "chunk rows keep the V swizzle");
@@ -122,7 +126,7 @@ __device__ __forceinline__ int seq_by_rank(const int32_t* kv_len, int B, int r, 
 }
 
 template <int D, int NW, bool PAGED, bool PARTIAL, int KS = 1>
-__global__ void __launch_bounds__(NW * 64, (PrefillCfg<D, NW, KS>::WG_PER_CU))
+__global__ void __launch_bounds__(NW * 64, (PrefillCfg<D, NW, KS>::MIN_WAVES_PER_SIMD))
 attn_prefill_kernel(const AttnArgs a) {
   using C = PrefillCfg<D, NW, KS>;
   constexpr int NTH = C::NTH;

@@ -215,7 +215,7 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
       // are taken only where that grid still fits one round, or where the
       // walk is long (32 or more 64-key tiles: the longest one allowed by
       // the split size or the key count).  Measured: ragged paged one pass
-      // (64 workgroups) 111 -> 70 us, with splits of 2048 72 -> 52 us, of
+      // (56 workgroups) 111 -> 70 us, with splits of 2048 72 -> 52 us, of
       // 1024 (256 workgroups, 16 tiles) 48 us kept; causal 2048^2 at
       // B = 1, Hkv = 8 (256 workgroups, 32 tiles) 62 -> 53 us; causal
       // 4096^2 there (512 workgroups) 137 -> 160 us with two groups, kept.

@@ -125,10 +125,13 @@ __device__ __forceinline__ int seq_by_rank(const int32_t* kv_len, int B, int r, 
   return r;  // not reached: ranks are a permutation of 0 .. B-1
 }
 
-template <int D, int NW, bool PAGED, bool PARTIAL, int KS = 1>
+// NT: a single q-tile per (b, kv head, split), so no other workgroup reads
+// this one's K/V tiles, which are then loaded with the non-temporal hint.
+template <int D, int NW, bool PAGED, bool PARTIAL, int KS, bool NT>
 __global__ void __launch_bounds__(NW * 64, (PrefillCfg<D, NW, KS>::MIN_WAVES_PER_SIMD))
 attn_prefill_kernel(const AttnArgs a) {
   using C = PrefillCfg<D, NW, KS>;
+  constexpr int CP = NT ? kCpNonTemporal : kCpDefault;
   constexpr int NTH = C::NTH;
   constexpr int BK = C::BK;
   constexpr int DC = C::DC;
@@ -270,8 +273,8 @@ attn_prefill_kernel(const AttnArgs a) {
                                   (valid - 1u) * vss2 + (uint32_t)D * 2u);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      st.k[i] = buf_load16v(kr, koff[i]);
-      st.v[i] = buf_load16v(vr, voff[i]);
+      st.k[i] = buf_load16v<CP>(kr, koff[i]);
+      st.v[i] = buf_load16v<CP>(vr, voff[i]);
     }
   };
   // the rows of a thread's chunks differ by multiples of 8: one swizzle

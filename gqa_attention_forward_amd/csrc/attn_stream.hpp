@@ -75,10 +75,13 @@ struct StreamCfg {
 // Q, O and the softmax state without spilling (a spill reload waits behind
 // the tile loads in flight), and this HBM-bound kernel streams fastest with
 // few, long-running waves per CU anyway.
-template <int D, int NQB, int NW, bool PAGED, bool PARTIAL>
+// NT: no other workgroup reads this one's K/V tiles (one q-tile), which
+// are then loaded with the non-temporal hint.
+template <int D, int NQB, int NW, bool PAGED, bool PARTIAL, bool NT>
 __global__ void __launch_bounds__(NW * 64, 1)
 attn_stream_kernel(const AttnArgs a) {
   using C = StreamCfg<D, NQB>;
+  constexpr int CP = NT ? kCpNonTemporal : kCpDefault;
   // tiles in flight per wave while it computes on one (a deeper rotation
   // measured no faster and needs one wave per SIMD)
   constexpr int DEPTH = 1;
@@ -244,9 +247,9 @@ attn_stream_kernel(const AttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16(kr, koff[kb] + 64u * c);
+      for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16<CP>(kr, koff[kb] + 64u * c);
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16(vr, voff + (uint32_t)j * vstep);
+    for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16<CP>(vr, voff + (uint32_t)j * vstep);
   };
   // the K (which = 0) or V (which = 1) half of `load`, for the late-issue order
   auto tile_res = [&](int j0, int which) {
@@ -267,12 +270,12 @@ attn_stream_kernel(const AttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16(kr, koff[kb] + 64u * c);
+      for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16<CP>(kr, koff[kb] + 64u * c);
   };
   auto load_v = [&](int j0, Tile& t) {
     const BufRes vr = tile_res(j0, 1);
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16(vr, voff, (uint32_t)j * vstep);
+    for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16<CP>(vr, voff, (uint32_t)j * vstep);
   };
 
   uint16_t* vbuf = smem + wv * C::VTILE;
@@ -568,10 +571,10 @@ attn_stream_kernel(const AttnArgs a) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-              tn.k[kb][c] = buf_load16(kr, (uint32_t)(16 * kb + c16) * ns2 + 64u * c + 16u * grp);
+              tn.k[kb][c] = buf_load16<CP>(kr, (uint32_t)(16 * kb + c16) * ns2 + 64u * c + 16u * grp);
 #pragma unroll
           for (int j = 0; j < VPL; ++j)
-            tn.v[j] = buf_load16(vr, (uint32_t)(lane / DC + j * (64 / DC)) * ns2 +
+            tn.v[j] = buf_load16<CP>(vr, (uint32_t)(lane / DC + j * (64 / DC)) * ns2 +
                                          16u * (lane % DC));
           // every key of the tile goes through the mask: key nl + r is
           // visible up to the row's causal bound, and rows r >= nnew not at all

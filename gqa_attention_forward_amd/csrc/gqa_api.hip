@@ -100,9 +100,10 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
                          int64_t q_rows_per_bg, int rows_per_tile, hipStream_t stream,
                          int lds_max = 0) {
   // dynamic LDS above 64 KiB has to be allowed once per kernel; the cache
-  // is keyed by the kernel address
+  // is keyed by the kernel address and holds every form the library builds
+  // (past its size the attribute would simply be set on every launch)
   static std::mutex mu;
-  static const void* done[64];
+  static const void* done[512];
   static int ndone = 0;
   {
     std::lock_guard<std::mutex> lock(mu);
@@ -113,7 +114,7 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
                                          lds_max > lds_bytes ? lds_max : lds_bytes);
       if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-      if (ndone < 64) done[ndone++] = reinterpret_cast<const void*>(kern);
+      if (ndone < 512) done[ndone++] = reinterpret_cast<const void*>(kern);
     }
   }
   args.n_qtiles = (int32_t)cdiv(q_rows_per_bg, rows_per_tile);
@@ -126,12 +127,23 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
   return check_launch("attention kernel");
 }
 
+// The non-temporal form where one q-tile covers the rows of a (b, kv head,
+// split).  Only the forms that can see several q-tiles are built in the
+// default form too: the 2- and 4-wave forms at d = 64 and 128 take at most
+// 64 and 128 rows, one q-tile, and two key groups run only above 128 rows.
 template <int D, int NW, bool PAGED, bool PARTIAL, int KS = 1>
 gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   using C = gqa::PrefillCfg<D, NW, KS>;
   args.spw = 1;
-  return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS>, C::LDS_BYTES, C::NT,
-                     args, rows, C::ROWS, stream);
+  if constexpr (KS == 1)
+    if (cdiv(rows, C::ROWS) == 1)
+      return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS, true>, C::LDS_BYTES,
+                         C::NT, args, rows, C::ROWS, stream);
+  if constexpr (NW == 8 || (NW == 4 && (D == 32 || D == 256)))
+    return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS, false>, C::LDS_BYTES,
+                       C::NT, args, rows, C::ROWS, stream);
+  return fail(GQA_ERR_UNSUPPORTED, "no prefill form for %lld rows at d = %d, %d waves",
+              (long long)rows, D, NW);
 }
 
 // Compute units of the current device (queried once per device).
@@ -150,12 +162,20 @@ int device_cus() {
   return cus[dev];
 }
 
+// The non-temporal form where one q-tile covers the group's rows; only 17-32
+// rows at d = 256 (one 16-column block per q-tile) take two.
 template <int D, int NQB, int NW, bool PAGED, bool PARTIAL>
 gqa_status_t launch_stream_nw(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   using C = gqa::StreamCfg<D, NQB>;
-  return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL>,
-                     C::lds_bytes(NW, PARTIAL ? args.spw : 0), NW * 64, args, rows, 16 * NQB,
-                     stream, C::lds_bytes(NW, PARTIAL ? C::max_spw(NW) : 0));
+  const int lds = C::lds_bytes(NW, PARTIAL ? args.spw : 0);
+  const int lds_max = C::lds_bytes(NW, PARTIAL ? C::max_spw(NW) : 0);
+  if (cdiv(rows, 16 * NQB) == 1)
+    return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL, true>, lds, NW * 64,
+                       args, rows, 16 * NQB, stream, lds_max);
+  if constexpr (D == 256 && NQB == 1)
+    return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL, false>, lds, NW * 64,
+                       args, rows, 16 * NQB, stream, lds_max);
+  return fail(GQA_ERR_UNSUPPORTED, "no stream form for %lld rows at d = %d", (long long)rows, D);
 }
 
 // Launch shape of the stream kernel.  Split-KV runs: each workgroup takes

@@ -82,9 +82,12 @@ __global__ void __launch_bounds__(NW * 64, 1)
 attn_stream_kernel(const AttnArgs a) {
   using C = StreamCfg<D, NQB>;
   constexpr int CP = NT ? kCpNonTemporal : kCpDefault;
-  // tiles in flight per wave while it computes on one (a deeper rotation
-  // measured no faster and needs one wave per SIMD)
-  constexpr int DEPTH = 1;
+  // tiles in flight per wave while it computes on one.  Two at d = 128 with
+  // one 16-column block (the decode form): the split-KV decode's partial
+  // kernel went from 81.5-82.8 to 79.5-80.8 us with its non-temporal loads.
+  // Elsewhere two spill (d = 256, and 32 columns at d = 128) or were not
+  // measured faster.
+  constexpr int DEPTH = (D == 128 && NQB == 1) ? 2 : 1;
   // At d = 256 a tile is 128 VGPRs, and Q and two whole tiles would not fit
   // the 256 arch VGPRs: the next tile's V loads are issued once the current
   // V is in LDS and its K loads once the current K has been through the

@@ -261,20 +261,34 @@ attn_prefill_kernel(const AttnArgs a) {
                                        : (int64_t)b * a.v_sb + (int64_t)g * a.v_sh);
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)a.page_table;
-  auto load_tile = [&](int j0, Stage& st) {
+  struct TileRes {
+    BufRes k, v;
+  };
+  auto tile_res = [&](int j0) {
     int64_t off;
     if constexpr (PAGED)
       off = (int64_t)ptab[(int64_t)b * a.max_pages + (j0 >> 6)] * a.kv_sp;
     else
       off = (int64_t)j0 * a.k_ss;
     const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
-    const BufRes kr = make_bufres(khead + off, (valid - 1u) * kss2 + (uint32_t)D * 2u);
-    const BufRes vr = make_bufres(vhead + (PAGED ? off : (int64_t)j0 * a.v_ss),
-                                  (valid - 1u) * vss2 + (uint32_t)D * 2u);
+    return TileRes{make_bufres(khead + off, (valid - 1u) * kss2 + (uint32_t)D * 2u),
+                   make_bufres(vhead + (PAGED ? off : (int64_t)j0 * a.v_ss),
+                               (valid - 1u) * vss2 + (uint32_t)D * 2u)};
+  };
+  auto load_k = [&](const TileRes& r, Stage& st) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) st.k[i] = buf_load16v<CP>(r.k, koff[i]);
+  };
+  auto load_v = [&](const TileRes& r, Stage& st) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) st.v[i] = buf_load16v<CP>(r.v, voff[i]);
+  };
+  auto load_tile = [&](int j0, Stage& st) {
+    const TileRes r = tile_res(j0);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      st.k[i] = buf_load16v<CP>(kr, koff[i]);
-      st.v[i] = buf_load16v<CP>(vr, voff[i]);
+      st.k[i] = buf_load16v<CP>(r.k, koff[i]);
+      st.v[i] = buf_load16v<CP>(r.v, voff[i]);
     }
   };
   // the rows of a thread's chunks differ by multiples of 8: one swizzle
@@ -289,6 +303,18 @@ attn_prefill_kernel(const AttnArgs a) {
       *reinterpret_cast<u32x4*>(Ks + kst + i * (NTH / DC) * C::KP) = st.k[i];
       *reinterpret_cast<u32x4*>(Vs + vst + i * (NTH / DC) * D) = st.v[i];
     }
+  };
+  auto store_k = [&](int stage, const Stage& st) {
+    uint16_t* Ks = sg + stage * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<u32x4*>(Ks + kst + i * (NTH / DC) * C::KP) = st.k[i];
+  };
+  auto store_v = [&](int stage, const Stage& st) {
+    uint16_t* Vs = sg + stage * C::STAGE + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<u32x4*>(Vs + vst + i * (NTH / DC) * D) = st.v[i];
   };
   // first key of this group's it-th tile
   auto tile_key = [&](int it) { return kbeg + (it * KS + kh) * BK; };
@@ -512,7 +538,11 @@ attn_prefill_kernel(const AttnArgs a) {
     const int j0 = tile_key(it);
     // Unconditional prefetch of the next tile (past the end it re-reads the
     // last tile, an L2 hit): no branch separates the loads from the compute.
-    load_tile(tile_key(min(it + 1, ntl - 1)), nx);
+    // Its K is loaded now and stored into the idle stage after the K^T Q
+    // phases; its V is loaded then and stored at the end, so only one
+    // tensor's chunks are held in registers at a time.
+    const TileRes nr = tile_res(tile_key(min(it + 1, ntl - 1)));
+    load_k(nr, nx);
     const uint16_t* Ks = sg + (it & 1) * C::STAGE;
     const uint16_t* Vs = Ks + C::KTILE;
     bf16x8 p0[2], p1[2];
@@ -525,15 +555,18 @@ attn_prefill_kernel(const AttnArgs a) {
     pin(p0);
     __builtin_amdgcn_sched_barrier(0);
     rescale(alpha0);
+    store_k((it + 1) & 1, nx);
+    load_v(nr, nx);
+    __builtin_amdgcn_sched_barrier(0);
     // 3. O += V_0 P_0 || softmax of S_1
     pv(Vs, 0, p0, True{});
     const float alpha1 = softmax(mask_tag, j0, 1, s1, p1);
     pin(p1);
     __builtin_amdgcn_sched_barrier(0);
     rescale(alpha1);
-    // 4. O += V_1 P_1, stage the next tile
+    // 4. O += V_1 P_1, stage the next tile's V
     pv(Vs, 1, p1, False{});
-    store_tile((it + 1) & 1, nx);
+    store_v((it + 1) & 1, nx);
     lds_barrier();
   };
 

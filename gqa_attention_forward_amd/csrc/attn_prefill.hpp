@@ -264,16 +264,19 @@ attn_prefill_kernel(const AttnArgs a) {
   struct TileRes {
     BufRes k, v;
   };
-  auto tile_res = [&](int j0) {
+  // `live` false: the prefetch past the last tile (it re-addresses that
+  // tile); its resources are empty, so the loads return zeros without
+  // touching memory, and the tile is never used.
+  auto tile_res = [&](int j0, bool live) {
     int64_t off;
     if constexpr (PAGED)
       off = (int64_t)ptab[(int64_t)b * a.max_pages + (j0 >> 6)] * a.kv_sp;
     else
       off = (int64_t)j0 * a.k_ss;
     const uint32_t valid = (uint32_t)min(BK, n - j0);  // >= 1: tiles start below kend <= n
-    return TileRes{make_bufres(khead + off, (valid - 1u) * kss2 + (uint32_t)D * 2u),
+    return TileRes{make_bufres(khead + off, live ? (valid - 1u) * kss2 + (uint32_t)D * 2u : 0u),
                    make_bufres(vhead + (PAGED ? off : (int64_t)j0 * a.v_ss),
-                               (valid - 1u) * vss2 + (uint32_t)D * 2u)};
+                               live ? (valid - 1u) * vss2 + (uint32_t)D * 2u : 0u)};
   };
   auto load_k = [&](const TileRes& r, Stage& st) {
 #pragma unroll
@@ -283,8 +286,8 @@ attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) st.v[i] = buf_load16v<CP>(r.v, voff[i]);
   };
-  auto load_tile = [&](int j0, Stage& st) {
-    const TileRes r = tile_res(j0);
+  auto load_tile = [&](int j0, Stage& st, bool live) {
+    const TileRes r = tile_res(j0, live);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       st.k[i] = buf_load16v<CP>(r.k, koff[i]);
@@ -321,7 +324,7 @@ attn_prefill_kernel(const AttnArgs a) {
 
   Stage nx;
   if (ntl > 0) {
-    load_tile(tile_key(0), nx);
+    load_tile(tile_key(0), nx, true);
     store_tile(0, nx);
   }
   lds_barrier();
@@ -504,7 +507,7 @@ attn_prefill_kernel(const AttnArgs a) {
   auto step_early = [&](auto mask_tag, int it, auto par) {
     constexpr int PAR = decltype(par)::value;
     const int j0 = tile_key(it);
-    load_tile(tile_key(min(it + 1, ntl - 1)), nx);
+    load_tile(tile_key(min(it + 1, ntl - 1)), nx, it + 1 < ntl);
     const uint16_t* Ks = sg + PAR * C::STAGE;
     const uint16_t* Vs = Ks + C::KTILE;
     bf16x8 k0[NCK], k1[NCK], v0[2 * NDB], v1[2 * NDB], p0[2], p1[2];
@@ -536,12 +539,12 @@ attn_prefill_kernel(const AttnArgs a) {
   };
   auto step = [&](auto mask_tag, int it) {
     const int j0 = tile_key(it);
-    // Unconditional prefetch of the next tile (past the end it re-reads the
-    // last tile, an L2 hit): no branch separates the loads from the compute.
+    // Unconditional prefetch of the next tile (past the end an empty one):
+    // no branch separates the loads from the compute.
     // Its K is loaded now and stored into the idle stage after the K^T Q
     // phases; its V is loaded then and stored at the end, so only one
     // tensor's chunks are held in registers at a time.
-    const TileRes nr = tile_res(tile_key(min(it + 1, ntl - 1)));
+    const TileRes nr = tile_res(tile_key(min(it + 1, ntl - 1)), it + 1 < ntl);
     load_k(nr, nx);
     const uint16_t* Ks = sg + (it & 1) * C::STAGE;
     const uint16_t* Vs = Ks + C::KTILE;

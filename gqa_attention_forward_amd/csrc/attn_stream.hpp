@@ -233,7 +233,10 @@ attn_stream_kernel(const AttnArgs a) {
   // scalar loads, which do not queue behind the tile loads in flight
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)a.page_table;
-  auto load = [&](int j0, Tile& t) {
+  // `live` false: a prefetch past the wave's last tile (it re-addresses that
+  // tile); its resources are empty, so the loads return zeros without
+  // touching memory, and the tile is never used.
+  auto load = [&](int j0, Tile& t, bool live) {
     const uint16_t *kp, *vp;
     if constexpr (PAGED) {
       const int pg = ptab[(int64_t)b * a.max_pages + (j0 >> 6)];
@@ -245,8 +248,8 @@ attn_stream_kernel(const AttnArgs a) {
       vp = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)j0 * a.v_ss;
     }
     const uint32_t valid = (uint32_t)min(BK, nl - j0);  // >= 1: tiles start below kend <= nl
-    const BufRes kr = make_bufres(kp, (valid - 1u) * kss2 + (uint32_t)D * 2u);
-    const BufRes vr = make_bufres(vp, (valid - 1u) * vss2 + (uint32_t)D * 2u);
+    const BufRes kr = make_bufres(kp, live ? (valid - 1u) * kss2 + (uint32_t)D * 2u : 0u);
+    const BufRes vr = make_bufres(vp, live ? (valid - 1u) * vss2 + (uint32_t)D * 2u : 0u);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -255,7 +258,7 @@ attn_stream_kernel(const AttnArgs a) {
     for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16<CP>(vr, voff + (uint32_t)j * vstep);
   };
   // the K (which = 0) or V (which = 1) half of `load`, for the late-issue order
-  auto tile_res = [&](int j0, int which) {
+  auto tile_res = [&](int j0, int which, bool live) {
     const uint16_t* p;
     if constexpr (PAGED) {
       const int pg = ptab[(int64_t)b * a.max_pages + (j0 >> 6)];
@@ -266,17 +269,17 @@ attn_stream_kernel(const AttnArgs a) {
                 : a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)j0 * a.k_ss;
     }
     const uint32_t valid = (uint32_t)min(BK, nl - j0);  // >= 1: tiles start below kend <= nl
-    return make_bufres(p, (valid - 1u) * (which ? vss2 : kss2) + (uint32_t)D * 2u);
+    return make_bufres(p, live ? (valid - 1u) * (which ? vss2 : kss2) + (uint32_t)D * 2u : 0u);
   };
-  auto load_k = [&](int j0, Tile& t) {
-    const BufRes kr = tile_res(j0, 0);
+  auto load_k = [&](int j0, Tile& t, bool live) {
+    const BufRes kr = tile_res(j0, 0, live);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16<CP>(kr, koff[kb] + 64u * c);
   };
-  auto load_v = [&](int j0, Tile& t) {
-    const BufRes vr = tile_res(j0, 1);
+  auto load_v = [&](int j0, Tile& t, bool live) {
+    const BufRes vr = tile_res(j0, 1, live);
 #pragma unroll
     for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16<CP>(vr, voff, (uint32_t)j * vstep);
   };
@@ -494,8 +497,9 @@ attn_stream_kernel(const AttnArgs a) {
 
   // ---- key loop: this wave takes tiles wv, wv + NW, ... of the run;
   // DEPTH + 1 register tiles in rotation.  The prefetch is unconditional
-  // (past the end it re-reads the wave's last tile, which is still in L2) so
-  // no branch sits between a load and the compute that must not wait for it.
+  // (past the end it addresses the wave's last tile through empty resources,
+  // so nothing is read) so no branch sits between a load and the compute
+  // that must not wait for it.
   // Splits are multiples of 64 keys, so no tile straddles two of them.  The
   // finished splits are flushed before the first tile of a later split, at a
   // point where that tile (and the DEPTH - 1 after it) is in flight and the
@@ -517,7 +521,7 @@ attn_stream_kernel(const AttnArgs a) {
     if (mine > 0) {
       Tile t[DEPTH + 1];
 #pragma unroll
-      for (int u = 0; u < DEPTH; ++u) load(tile_key(u), t[u]);
+      for (int u = 0; u < DEPTH; ++u) load(tile_key(u), t[u], u < mine);
       // The exit leaves both loops at once: a path back through the loop
       // head with a prefetched tile left unconsumed would make the compiler
       // wait for that tile on every iteration.
@@ -528,7 +532,7 @@ attn_stream_kernel(const AttnArgs a) {
           enter(k + u);
           Tile& nx = t[(u + DEPTH) % (DEPTH + 1)];
           if constexpr (!LATE) {
-            load(tile_key(k + u + DEPTH), nx);
+            load(tile_key(k + u + DEPTH), nx, k + u + DEPTH < mine);
             // keep the prefetch ahead of the first wait on tile k + u
             __builtin_amdgcn_sched_barrier(0);
             stage_v(t[u]);
@@ -536,12 +540,12 @@ attn_stream_kernel(const AttnArgs a) {
           } else {
             // next V once this V is in LDS, next K once this K has been used
             stage_v(t[u]);
-            load_v(tile_key(k + u + DEPTH), nx);
+            load_v(tile_key(k + u + DEPTH), nx, k + u + DEPTH < mine);
             __builtin_amdgcn_sched_barrier(0);
             f32x4 s[NQB][2];
             qk(t[u], s);
             __builtin_amdgcn_sched_barrier(0);
-            load_k(tile_key(k + u + DEPTH), nx);
+            load_k(tile_key(k + u + DEPTH), nx, k + u + DEPTH < mine);
             __builtin_amdgcn_sched_barrier(0);
             finish(tile_key(k + u), s);
           }

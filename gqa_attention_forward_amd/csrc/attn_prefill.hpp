@@ -455,10 +455,12 @@ attn_prefill_kernel(const AttnArgs a) {
 
   // Whole-phase operand fetches (EARLY): each phase's LDS operands are
   // requested before the previous phase's MFMAs, so none of its MFMAs waits
-  // on LDS latency.  Needs 2 x D / 4 more VGPRs; only the 8-wave form at
-  // d <= 128 has them, and with two key groups (twice the staging registers)
-  // only at d = 64: at d = 128 that form spills.
-  constexpr bool EARLY = (NW == 8 && D <= 128 && (KS == 1 || D <= 64));
+  // on LDS latency.  Needs 2 x D / 4 more VGPRs: the 8-wave form at d <= 128
+  // has them, with two key groups (twice the staging registers) only at
+  // d = 64, and the 4-wave form at d <= 64.  At d = 128 those two forms
+  // spill with it.
+  constexpr bool EARLY =
+      (NW == 8 && D <= 128 && (KS == 1 || D <= 64)) || (NW == 4 && D <= 64);
   auto kfetch = [&](const uint16_t* Ks, int h, bf16x8 (&k)[NCK]) {
 #pragma unroll
     for (int c = 0; c < NCK; ++c) k[c] = kread(Ks, c, h);
@@ -577,7 +579,8 @@ attn_prefill_kernel(const AttnArgs a) {
   if constexpr (EARLY) {
     // Tiles two at a time (stages 0 and 1), unmasked tiles first, then the
     // masked ones; a leftover single tile runs on its own stage.  (The
-    // smaller forms keep a runtime stage: unrolled, they would spill.)
+    // forms without the early fetch keep a runtime stage: unrolled, they
+    // would spill.)
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     for (; it + 1 < nfull; it += 2) {

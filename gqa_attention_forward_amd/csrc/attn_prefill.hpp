@@ -457,10 +457,10 @@ attn_prefill_kernel(const AttnArgs a) {
   // requested before the previous phase's MFMAs, so none of its MFMAs waits
   // on LDS latency.  Needs 2 x D / 4 more VGPRs: the 8-wave form at d <= 128
   // has them, with two key groups (twice the staging registers) only at
-  // d = 64, and the 4-wave form at d <= 64.  At d = 128 those two forms
+  // d = 64, and the 2- and 4-wave forms at d <= 64.  At d = 128 those forms
   // spill with it.
   constexpr bool EARLY =
-      (NW == 8 && D <= 128 && (KS == 1 || D <= 64)) || (NW == 4 && D <= 64);
+      (NW == 8 && D <= 128 && (KS == 1 || D <= 64)) || (NW <= 4 && D <= 64);
   auto kfetch = [&](const uint16_t* Ks, int h, bf16x8 (&k)[NCK]) {
 #pragma unroll
     for (int c = 0; c < NCK; ++c) k[c] = kread(Ks, c, h);

@@ -213,6 +213,15 @@ gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
 // registers without spilling.
 template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
+  // At d <= 64 the 2-wave shared-tile form streams groups of up to 64 rows
+  // faster than the stream kernel, whose 32-key tiles carry few bytes per
+  // step there (B 16, Hkv 8, 8192 keys, splits of 1024: decode 53 -> 45 us
+  // at d = 64 and 43 -> 31 us at d = 32; 32-row groups 79 -> 55 us and
+  // 65 -> 35 us).  The fused append and the in-kernel merge live in the
+  // stream kernel only.
+  if constexpr (D <= 64)
+    if (rows <= 64 && !args.k_new && !args.tickets)
+      return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
   if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
   if (rows <= 32) {
     // two 16-column blocks of Q do not fit beside the d = 256 tiles: two q-tiles

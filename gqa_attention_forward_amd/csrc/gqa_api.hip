@@ -213,15 +213,25 @@ gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
 // registers without spilling.
 template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  // At d <= 64 the 2-wave shared-tile form streams groups of up to 64 rows
-  // faster than the stream kernel, whose 32-key tiles carry few bytes per
-  // step there (B 16, Hkv 8, 8192 keys, splits of 1024: decode 53 -> 45 us
-  // at d = 64 and 43 -> 31 us at d = 32; 32-row groups 79 -> 55 us and
-  // 65 -> 35 us).  The fused append and the in-kernel merge live in the
-  // stream kernel only.
-  if constexpr (D <= 64)
-    if (rows <= 64 && !args.k_new && !args.tickets)
+  // Short groups on the shared-tile prefill form, where its grid (one
+  // workgroup per (b, kv head, split)) fills the CUs at least twice: at
+  // d <= 64 every group of up to 64 rows, whose 32-key stream tiles carry
+  // few bytes per step; at d = 128 and 256 the groups of 17-32 rows (two
+  // 16-column blocks, or at d = 256 two q-tiles reading K/V twice).
+  // Measured at B 16, Hkv 8, 8192 keys, splits of 1024: decode 52 -> 48 us
+  // at d = 64; 32-row groups 112-123 -> 101-102 us at d = 128 and 382 ->
+  // 219 us at d = 256.  Smaller grids keep the stream kernel, whose launch
+  // shape adapts to them (B 1 decode at d = 64: 18 us, 24 us routed).  The
+  // fused append and the in-kernel merge live in the stream kernel only.
+  if (rows <= 64 && !args.k_new && !args.tickets &&
+      (int64_t)args.B * args.Hkv * args.n_split >= 2 * (int64_t)device_cus()) {
+    if constexpr (D <= 64) {
       return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
+    } else if (rows > 16 && rows <= 32) {
+      if constexpr (D == 128) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
+      if constexpr (D == 256) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
+    }
+  }
   if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
   if (rows <= 32) {
     // two 16-column blocks of Q do not fit beside the d = 256 tiles: two q-tiles

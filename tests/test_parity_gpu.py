@@ -447,6 +447,43 @@ def test_prefill_key_group_boundary(case, causal, tile):
     assert_close(out[bi, hi, ii], want, f"key groups case={case} causal={causal} tile={tile}")
 
 
+# Short query groups go to the shared-tile prefill form when the grid (B x
+# Hkv x splits) fills the 256 CUs at least twice: every group of up to 64
+# rows at d <= 64, and 17-32 rows at d = 128 and 256.  These shapes reach
+# that grid (B, Hq, Hkv, Sq, Skv, d, split size); the last one stays below it.
+SHORT_GROUP_CASES = [
+    (16, 32, 8, 1, 2048, 64, 256),    # d = 64 decode, 1024 workgroups
+    (8, 32, 8, 8, 2048, 32, 256),     # d = 32, 32-row groups
+    (8, 32, 8, 8, 2048, 128, 256),    # d = 128, 32-row groups
+    (8, 64, 8, 3, 1024, 256, 128),    # d = 256, 24-row groups
+    (2, 32, 8, 1, 2048, 64, 256),     # d = 64 decode, 128 workgroups: stream kernel
+]
+
+
+@pytest.mark.parametrize("case", range(len(SHORT_GROUP_CASES)))
+def test_short_groups_large_grid(case):
+    B, Hq, Hkv, Sq, Skv, d, tile = SHORT_GROUP_CASES[case]
+    note(f"short groups B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} d={d} tile={tile}")
+    inp = workloads.make_dense(B, Hq, Hkv, Sq, Skv, d, seed=90 + case, kv_len="random", sink=True,
+                               nan_pad=True)
+    for causal in ([False, True] if Sq > 1 else [False]):
+        want = oracle_dense(inp, causal=causal)
+        assert_close(run_dense(inp, causal=causal, tile=tile), want,
+                     f"short groups case={case} causal={causal}")
+        if Sq == 1:
+            assert_close(run_dense(inp, tile=tile, decode=True), want, f"decode case={case}")
+
+
+def test_paged_decode_large_grid_d64():
+    """Paged decode at d = 64 over 64 sequences (4096 workgroups of splits):
+    the shared-tile form, page-table addressing, ragged kv_len, sink."""
+    note("paged decode d=64, 64 sequences, splits of 256")
+    rng = np.random.default_rng(11)
+    kv = [int(x) for x in rng.integers(1, 2048, 64)]
+    w = workloads.make_paged(B=64, Hq=32, Hkv=8, d=64, q_lens=[1] * 64, kv_lens=kv, seed=12)
+    assert_close(_paged_run(w, tile=256), _paged_oracle(w), "paged decode d=64 large grid")
+
+
 @pytest.mark.parametrize("Skv", [1, 63, 1024, 3000])
 def test_decode_sweep(Skv):
     note(f"decode Skv={Skv}")

@@ -218,16 +218,20 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
   // d <= 64 every group of up to 64 rows, whose 32-key stream tiles carry
   // few bytes per step; at d = 128 and 256 the groups of 17-32 rows (two
   // 16-column blocks, or at d = 256 two q-tiles reading K/V twice).
+  // Paged decode at d = 128 too: its 64-key tiles are whole pages.
   // Measured at B 16, Hkv 8, 8192 keys, splits of 1024: decode 52 -> 48 us
   // at d = 64; 32-row groups 112-123 -> 101-102 us at d = 128 and 382 ->
-  // 219 us at d = 256.  Smaller grids keep the stream kernel, whose launch
-  // shape adapts to them (B 1 decode at d = 64: 18 us, 24 us routed).  The
-  // fused append and the in-kernel merge live in the stream kernel only.
+  // 219 us at d = 256; paged decode at d = 128 98-100 -> 92-95 us (dense
+  // decode there stays faster on the stream kernel, 82 against 88 us, and
+  // so does paged decode at d = 256, 173 against 198 us).  Smaller grids
+  // keep the stream kernel, whose launch shape adapts to them (B 1 decode
+  // at d = 64: 18 us, 24 us routed).  The fused append and the in-kernel
+  // merge live in the stream kernel only.
   if (rows <= 64 && !args.k_new && !args.tickets &&
       (int64_t)args.B * args.Hkv * args.n_split >= 2 * (int64_t)device_cus()) {
     if constexpr (D <= 64) {
       return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
-    } else if (rows > 16 && rows <= 32) {
+    } else if ((PAGED && D == 128 && rows <= 16) || (rows > 16 && rows <= 32)) {
       if constexpr (D == 128) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
       if constexpr (D == 256) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
     }

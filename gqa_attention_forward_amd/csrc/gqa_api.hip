@@ -130,12 +130,13 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
 // The non-temporal form where one q-tile covers the rows of a (b, kv head,
 // split).  Only the forms that can see several q-tiles are built in the
 // default form too: the 2- and 4-wave forms at d = 64 and 128 take at most
-// 64 and 128 rows, one q-tile, and two key groups run only above 128 rows.
+// 64 and 128 rows, one q-tile.  Two key groups take one q-tile only for
+// 65-128 rows at d = 128.
 template <int D, int NW, bool PAGED, bool PARTIAL, int KS = 1>
 gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
   using C = gqa::PrefillCfg<D, NW, KS>;
   args.spw = 1;
-  if constexpr (KS == 1)
+  if constexpr (KS == 1 || D == 128)
     if (cdiv(rows, C::ROWS) == 1)
       return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS, true>, C::LDS_BYTES,
                          C::NT, args, rows, C::ROWS, stream);
@@ -203,10 +204,13 @@ gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
   return launch_stream_nw<D, NQB, 2, PAGED, PARTIAL>(args, rows, stream);
 }
 
-// Kernel choice by query rows per (b, kv head): groups of up to 32 rows
-// (decode, short query blocks) stream keys per wave; larger groups share
-// K/V tiles across the waves of a workgroup, 32 rows per wave.
-// The prefill kernel's widths per head dim: a 64-key tile splits into whole
+// Kernel choice by query rows per (b, kv head) and grid size.  Groups of up
+// to 32 rows (decode, short query blocks) stream keys per wave in the
+// stream kernel; larger groups share K/V tiles across the waves of a
+// workgroup, 32 rows per wave (the prefill kernel).  On grids that fill the
+// CUs twice or more the shared-tile form takes some short groups too, and on
+// grids that fit them in one round it splits a workgroup's keys between two
+// wave groups (both below).  The prefill kernel's widths per head dim: a 64-key tile splits into whole
 // 16-byte chunks per thread from 2 waves up at d = 32 only up to 4 waves; the
 // V swizzle needs 4 or more waves at d = 256, where one workgroup per CU
 // with 4 waves (one per SIMD) holds the 32-row O and Q of a wave in
@@ -248,6 +252,15 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
     return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
   } else {
     if (rows <= 64) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
+    if constexpr (D == 128) {
+      // 65-128 rows on a grid that fits the CUs in one round: the 8-wave
+      // form with two key groups over the 128 rows halves each workgroup's
+      // walk (short-q, B 16, Hkv 4, 16384 keys: one pass 350 -> 240 us,
+      // splits of 4096 122-142 -> 101-111 us; with splits of 2048, 512
+      // workgroups, the 4-wave form two per CU is as fast)
+      if (rows <= 128 && (int64_t)args.B * args.Hkv * args.n_split <= device_cus())
+        return launch_prefill<D, 8, PAGED, PARTIAL, 2>(args, rows, stream);
+    }
     if (D == 32 || rows <= 128) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
     if constexpr (D != 32) {
       // The 8-wave form holds one workgroup per CU.  A grid that fits the

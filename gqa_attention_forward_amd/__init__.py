@@ -29,11 +29,21 @@ __all__ = ["prefill", "decode_splitkv", "splitkv_partial", "splitkv_merge", "pag
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # plain ints: the argtypes (c_void_p) convert them, None passes NULL
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+# the current stream's raw handle: torch's own accessor where it has one
+# (about 1.5 us less per call than building a Stream object), else the
+# public call
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else
+                           torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _need_dev(name, t, dtype):

@@ -121,5 +121,8 @@ def check(status: int) -> None:
     raise _EXC.get(status, GQAError)(status, msg)
 
 
+_I64x3 = ctypes.c_int64 * 3
+
+
 def strides3(values) -> ctypes.Array:
-    return (ctypes.c_int64 * 3)(*[int(x) for x in values])
+    return _I64x3(int(values[0]), int(values[1]), int(values[2]))

@@ -660,6 +660,7 @@ attn_prefill_kernel(const AttnArgs a) {
       row = ((int64_t)b * a.Hq + hq) * a.Sq + pq;
     const int64_t idx = row * a.n_split + split;
     if (hl == 0) a.ws_ml[idx] = make_float2(mtrue == -INFINITY ? -INFINITY : mtrue * kLn2, lt);
+    if (a.skip_empty_o && mtrue == -INFINITY) return;  // no visible key in this split
     float* op = a.ws_o + idx * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -83,6 +83,10 @@ struct AttnArgs {
   // in-kernel merge (stream kernel, partial mode): one ticket per (b, kv
   // head, q-tile), zero on entry and left zero; nullptr = merge kernel
   int32_t* tickets;
+  // partial mode, shared-tile kernel: an empty state's O~ (all zeros) is left
+  // unwritten; set only where the library's own merge, which gives such a
+  // state weight 0 without reading it, follows
+  int32_t skip_empty_o;
 };
 
 // Raw buffer resource (CDNA: stride 0, no swizzle, third dword 0x00020000).

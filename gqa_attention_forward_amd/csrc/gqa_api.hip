@@ -301,7 +301,7 @@ gqa_status_t dispatch(gqa::AttnArgs args, int d, int64_t rows, hipStream_t strea
 
 gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int32_t B,
                           int32_t Hq, int32_t Sq, int32_t d, int32_t n_split, const float* sink,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool sparse = false) {
   const int64_t rows = (int64_t)B * Hq * Sq;
   if (rows == 0) return GQA_OK;
   const float2* ml = reinterpret_cast<const float2*>(workspace);
@@ -310,10 +310,14 @@ gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int
   const int64_t nblocks = cdiv(rows, 4);
   if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   (void)hipGetLastError();
-  auto kern = d == 32 ? gqa::merge_kernel<32>
-              : d == 64 ? gqa::merge_kernel<64>
-              : d == 128 ? gqa::merge_kernel<128>
-                         : gqa::merge_kernel<256>;
+  auto kern = sparse ? (d == 32 ? gqa::merge_kernel<32, true>
+                        : d == 64 ? gqa::merge_kernel<64, true>
+                        : d == 128 ? gqa::merge_kernel<128, true>
+                                   : gqa::merge_kernel<256, true>)
+                     : (d == 32 ? gqa::merge_kernel<32, false>
+                        : d == 64 ? gqa::merge_kernel<64, false>
+                        : d == 128 ? gqa::merge_kernel<128, false>
+                                   : gqa::merge_kernel<256, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(256), 0, stream, ml, ot,
                      reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq, n_split,
                      rows);
@@ -448,9 +452,14 @@ gqa_status_t gqa_attention_prefill(const void* q, const int64_t q_stride[3], con
     GQA_TRY(dispatch<false, false>(a, d, (int64_t)Sq * a.G, st));
     return ok();
   }
+  // the merge below gives empty states weight 0 without reading their O~;
+  // groups of more than 64 rows with causal or per-batch lengths have many
+  // (the sparse merge then reads only the states that hold keys)
+  a.skip_empty_o = 1;
   GQA_TRY(run_partial(a, d, tile_s_kv, workspace, st));
+  const bool sparse = (int64_t)Sq * a.G > 64 && (causal || kv_len);
   GQA_TRY(launch_merge(workspace, o, o_stride, B, Hq, Sq, d, a.Skv > 0 ? (int32_t)cdiv(Skv, tile_s_kv) : 1,
-                       sink, st));
+                       sink, st, sparse));
   return ok();
 }
 
@@ -631,10 +640,13 @@ gqa_status_t paged_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   a.ws_ml = reinterpret_cast<float2*>(workspace);
   a.ws_o = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                     (size_t)Hq * total_q * n_split * 8);
+  // as for the dense split path: ragged sequences leave many states empty
+  a.skip_empty_o = 1;
   GQA_TRY(dispatch<true, true>(a, d, rows, st));
   // partial rows are h * total_q + t: the merge sees B = 1, Sq = total_q
   const int64_t mo[3] = {0, o_stride_h, o_stride_t};
-  GQA_TRY(launch_merge(workspace, o, mo, 1, Hq, total_q, d, (int32_t)n_split, sink, st));
+  GQA_TRY(launch_merge(workspace, o, mo, 1, Hq, total_q, d, (int32_t)n_split, sink, st,
+                       rows > 64));
   return ok();
 }
 

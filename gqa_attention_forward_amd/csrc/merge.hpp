@@ -8,8 +8,10 @@ namespace gqa {
 // Split-KV merge (kernbench2 benches commit log: the (m, l, O) state and its
 // associative merge; nvfp4-megamoe-kernel commit log: normalise once).
 // One 64-lane wave per query row; D / 64 output elements per lane (one per
-// lane of the first 32 at d = 32).
-template <int D>
+// lane of the first 32 at d = 32).  SPARSE: a state's O~ is read only when
+// its m is finite (where many splits are empty: causal or ragged rows over
+// large groups); otherwise all loads of a round issue together.
+template <int D, bool SPARSE>
 __global__ void __launch_bounds__(256)
 merge_kernel(const float2* __restrict__ ml, const float* __restrict__ ot, uint16_t* o,
              int64_t o_sb, int64_t o_sh, int64_t o_ss, const float* sink, int Hq, int Sq,
@@ -40,8 +42,18 @@ merge_kernel(const float2* __restrict__ ml, const float* __restrict__ ot, uint16
     for (int j = 0; j < CH; ++j) {
       const int s = min(s0 + j, n_split - 1);  // branch-free: duplicates are dropped below
       st[j] = mlr[s];
+      if constexpr (!SPARSE) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) ov[j][e] = otr[(int64_t)s * D + e];
+        for (int e = 0; e < E; ++e) ov[j][e] = otr[(int64_t)s * D + e];
+      }
+    }
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const bool live = s0 + j < n_split && st[j].x != -INFINITY;  // wave-uniform
+#pragma unroll
+        for (int e = 0; e < E; ++e) ov[j][e] = live ? otr[(int64_t)(s0 + j) * D + e] : 0.f;
+      }
     }
     float mc = M;
 #pragma unroll

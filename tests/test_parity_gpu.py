@@ -484,6 +484,39 @@ def test_paged_decode_large_grid_d64():
     assert_close(_paged_run(w, tile=256), _paged_oracle(w), "paged decode d=64 large grid")
 
 
+@pytest.mark.parametrize("Sq,G,causal", [(8, 8, True), (48, 4, True), (24, 8, False), (6, 8, False)])
+def test_split_workspace_full_of_nan(Sq, G, causal):
+    """The library's split paths leave an empty state's O~ unwritten and their
+    merge must never read it: with the workspace filled with NaN bytes first,
+    the result still matches the oracle.  Groups of 48-192 rows with per-batch
+    lengths (the sparse merge above 64 rows, the dense one below), dense and
+    paged."""
+    note(f"NaN-filled workspace Sq={Sq} G={G} causal={causal}")
+    B, Hkv, Skv, d, tile = 3, 2, 700, 64, 128
+    inp = workloads.make_dense(B, Hkv * G, Hkv, Sq, Skv, d, seed=120 + Sq, kv_len="random",
+                               sink=True, nan_pad=True)
+    g = to_dev(inp)
+    m = gqa()
+    ws = torch.full((m.workspace_size(B, Hkv * G, Sq, Skv, d, tile),), 255, dtype=torch.uint8,
+                    device=dev())
+    out = m.prefill(g["q"], g["k"], g["v"], kv_len=g["kv_len"], scale=inp["scale"],
+                    sink=g["sink"], causal=causal, tile_s_kv=tile, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().numpy(), oracle_dense(inp, causal=causal), "dense, NaN workspace")
+    q_lens = [max(1, Sq - 3 * b) for b in range(B)]
+    w = workloads.make_paged(B=B, Hq=Hkv * G, Hkv=Hkv, d=d, q_lens=q_lens,
+                             kv_lens=[max(q, 100 + 250 * b) for b, q in enumerate(q_lens)],
+                             seed=130 + Sq)
+    gw = to_dev(w)
+    wsp = torch.full((m.workspace_size(1, Hkv * G, w["total_q"], w["page_table"].shape[1] * 64, d,
+                                       tile),), 255, dtype=torch.uint8, device=dev())
+    outp = m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"], gw["page_table"],
+                   gw["kv_len"], max_q_len=w["max_q_len"], scale=w["scale"], sink=gw["sink"],
+                   causal=causal, tile_s_kv=tile, workspace=wsp)
+    torch.cuda.synchronize()
+    assert_close(outp.float().cpu().numpy(), _paged_oracle(w, causal=causal), "paged, NaN workspace")
+
+
 @pytest.mark.parametrize("Skv", [1, 63, 1024, 3000])
 def test_decode_sweep(Skv):
     note(f"decode Skv={Skv}")

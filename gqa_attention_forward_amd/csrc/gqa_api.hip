@@ -99,22 +99,26 @@ template <class K>
 gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args,
                          int64_t q_rows_per_bg, int rows_per_tile, hipStream_t stream,
                          int lds_max = 0) {
-  // dynamic LDS above 64 KiB has to be allowed once per kernel; the cache
-  // is keyed by the kernel address and holds every form the library builds
-  // (past its size the attribute would simply be set on every launch)
+  // dynamic LDS above 64 KiB has to be allowed once per kernel and device;
+  // the cache is keyed by both and holds every form the library builds on a
+  // few devices (past its size the attribute would simply be set on every
+  // launch)
   static std::mutex mu;
-  static const void* done[512];
+  static struct { const void* kern; int dev; } done[1024];
   static int ndone = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   {
     std::lock_guard<std::mutex> lock(mu);
     bool seen = false;
-    for (int i = 0; i < ndone; ++i) seen |= done[i] == reinterpret_cast<const void*>(kern);
+    for (int i = 0; i < ndone; ++i)
+      seen |= done[i].kern == reinterpret_cast<const void*>(kern) && done[i].dev == dev;
     if (!seen) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
                                          lds_max > lds_bytes ? lds_max : lds_bytes);
       if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-      if (ndone < 512) done[ndone++] = reinterpret_cast<const void*>(kern);
+      if (ndone < 1024) done[ndone++] = {reinterpret_cast<const void*>(kern), dev};
     }
   }
   args.n_qtiles = (int32_t)cdiv(q_rows_per_bg, rows_per_tile);

@@ -113,6 +113,10 @@ const char* gqa_last_error(void);
  * sum_j exp(s_j - m_s) v_j (nvfp4-megamoe-kernel commit log, multi-tile FA2
  * commit: P stays un-normalised; kernbench2 benches commit log, tile-granular
  * ring-KV commit: the persistent (m, l, O) state).
+ * gqa_attention_splitkv_partial writes every state (O~ = 0 for an empty one).
+ * After gqa_attention_prefill or gqa_attention_paged with tile_s_kv > 0 the
+ * workspace is scratch: an empty state's O~ may be left unwritten there, as
+ * the library's merge gives it weight 0 without reading it.
  */
 gqa_status_t gqa_attention_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv,
                                           int64_t d, int32_t tile_s_kv, size_t* bytes);

@@ -170,7 +170,7 @@ def time_cold(fn, stream, flush, min_iters=50, min_ms=200.0):
 
 # Kernel sources behind the split-KV partial kernel; the committed counter
 # summary records their hash.
-PARTIAL_SOURCES = ("attn_stream.hpp", "common.hpp", "gqa_api.hip")
+PARTIAL_SOURCES = ("attn_stream.hpp", "common.hpp", "launch.hpp", "gqa_api.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_partial_hbm_traffic.txt")
 
 

@@ -4,8 +4,10 @@
 // Each workgroup owns one (b, kv head g, q-tile) and a run of `spw`
 // consecutive kv splits.  Its NW waves cut the run's keys into 32-key tiles
 // taken round-robin, and each wave streams its tiles on its own.  A wave
-// keeps the next tile's K and V in flight in registers while it computes on
-// the current one.  When a wave's next tile belongs to a later split, the
+// keeps the next tile's K and V (two tiles in the d = 128 decode form) in
+// flight in registers while it computes on the current one; where one
+// q-tile covers the group, no other workgroup reads those tiles and the
+// loads carry the non-temporal hint (NT).  When a wave's next tile belongs to a later split, the
 // waves' running states (m, l, O) are combined through LDS (the associative
 // (m, l, O) merge of the kernbench2 2-D mesh all-reduce-mlo commit) and
 // written as that split's partial (or as the final normalised output when

@@ -1,5 +1,7 @@
-// Host side of libgqa: argument validation, work planning and kernel launch
-// behind the C ABI declared in include/gqa.h.
+// Host side of libgqa: the C ABI declared in include/gqa.h, argument
+// validation and the merge launch.  The attention kernels' launch and the
+// per-call choice of kernel form are in launch.hpp (instantiated per head
+// dim in dispatch_d*.hip).
 //
 // Validation follows the AstrAI commit log's binding checks (q-head/kv-head
 // divisibility, head-dim contiguity, split-KV scratch layout validated before

@@ -1,6 +1,7 @@
-// Prefill GQA forward kernel: query groups of more than 32 rows per
-// (b, kv head).  One workgroup per (b, kv head g, q-tile of 32 * NW rows,
-// kv split); all NW waves share each 64-key K/V tile through LDS, so a tile
+// Shared-tile GQA forward kernel: query groups of more than 32 rows per
+// (b, kv head), and shorter groups on grids large enough (launch.hpp).  One
+// workgroup per (b, kv head g, q-tile of 32 * NW / KS rows, kv split); its
+// waves share each 64-key K/V tile through LDS, so a tile
 // is fetched once per workgroup for every query head of the group (AstrAI
 // commit log, the commit that packs HB = min(G, warps) query heads per
 // block).  Each wave owns 32 query rows.  The 8-wave form (d = 64, 128)

@@ -143,7 +143,8 @@ gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int
   const float* ot = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
                                                    (size_t)rows * n_split * 8);
   const int64_t nblocks = cdiv(rows, 4);
-  if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  if (nblocks * 256 > 0xffffffffLL)  // work-items of one dispatch: 32 bits
+    return fail(GQA_ERR_UNSUPPORTED, "merge grid too large (%lld rows)", (long long)rows);
   (void)hipGetLastError();
   auto kern = sparse ? (d == 32 ? gqa::merge_kernel<32, true>
                         : d == 64 ? gqa::merge_kernel<64, true>
@@ -276,7 +277,6 @@ gqa_status_t gqa_attention_prefill(const void* q, const int64_t q_stride[3], con
   if (tile_s_kv > 0)
     need = workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d);
   GQA_TRY(check_workspace(workspace, workspace_bytes, need));
-  if (rows == 0) return ok();
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   gqa::AttnArgs a = dense_args(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv,
                                kv_len, scale, causal);
@@ -356,7 +356,6 @@ gqa_status_t gqa_attention_splitkv_partial(const void* q, const int64_t q_stride
   if (rows == 0) return ok();
   const size_t need = workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d);
   GQA_TRY(check_workspace(workspace, workspace_bytes, need));
-  if (rows == 0) return ok();
   gqa::AttnArgs a = dense_args(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, Sq, Skv,
                                kv_len, scale, causal);
   GQA_TRY(run_partial(a, d, tile_s_kv, workspace, reinterpret_cast<hipStream_t>(stream)));

@@ -48,7 +48,9 @@ gqa_status_t launch_grid(K* kern, int lds_bytes, int threads, gqa::AttnArgs args
   if (args.spw < 1) args.spw = 1;
   const int64_t nblocks = (int64_t)args.B * args.Hkv * cdiv(args.n_split, args.spw) * args.n_qtiles;
   if (nblocks <= 0) return GQA_OK;
-  if (nblocks > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large (%lld)", (long long)nblocks);
+  // the dispatch packet counts work-items in 32 bits
+  if (nblocks * threads > 0xffffffffLL)
+    return fail(GQA_ERR_UNSUPPORTED, "grid too large (%lld workgroups)", (long long)nblocks);
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(threads), lds_bytes, stream, args);
   return check_launch("attention kernel");

@@ -52,7 +52,8 @@
  *    kv_stride_row) must be below 2^26 elements, else GQA_ERR_UNSUPPORTED.
  *    d must be 32, 64, 128 or 256, else GQA_ERR_UNSUPPORTED (the AstrAI
  *    commit log's kernels cover prefill at head dim 32 and decode at 256
- *    besides 64 and 128).
+ *    besides 64 and 128).  A launch whose grid would exceed 2^32 - 1
+ *    work-items (one dispatch's limit) also returns GQA_ERR_UNSUPPORTED.
  *
  * Ownership: the caller owns all memory and keeps it alive until the work
  * enqueued on `stream` completes.  The library never allocates, frees,
@@ -87,7 +88,8 @@ typedef int32_t gqa_status_t;
 #define GQA_OK 0
 #define GQA_ERR_INVALID_ARGUMENT 1 /* NULL required pointer, bad dims, Hq % Hkv != 0, bad flag */
 #define GQA_ERR_UNSUPPORTED 2      /* d not 32/64/128/256, misaligned pointer or stride,
-                                      page_size != 64, a group beyond the append/fused limits */
+                                      page_size != 64, a group beyond the append/fused limits,
+                                      a grid beyond 2^32 - 1 work-items */
 #define GQA_ERR_WORKSPACE 3        /* workspace NULL or too small; ticket array too small */
 #define GQA_ERR_HIP 4              /* a HIP launch failed; message from hipGetErrorString */
 

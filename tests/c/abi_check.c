@@ -82,6 +82,11 @@ int main(void) {
   expect("merge n_split 0",
          gqa_attention_splitkv_merge(P, 1 << 20, P, s, 2, 8, 3, 64, 0, NULL, NULL),
          GQA_ERR_INVALID_ARGUMENT);
+  /* 64 heads x 2^26 rows: 2^30 merge workgroups of 256 work-items, more
+   * than one dispatch can count */
+  expect("merge grid beyond 2^32 work-items",
+         gqa_attention_splitkv_merge(P, SIZE_MAX, P, s, 1, 64, 1 << 26, 64, 1, NULL, NULL),
+         GQA_ERR_UNSUPPORTED);
 #define PAGED(cu, pt, kvl, page, d, causal) \
   gqa_attention_paged(P, 4096, 128, cu, P, P, 8192, 128, 128, pt, 64, kvl, P, 4096, 128, 8, 32, \
                       1, d, page, 100, 64, 0.088f, NULL, causal, 0, NULL, 0, NULL)

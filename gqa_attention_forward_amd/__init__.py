@@ -46,17 +46,47 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _need_dev(name, t, dtype):
+def _need_dev(name, t, dtype, device=None):
     if t is None:
         return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the query on {device}")
 
 
-def _bhsd(name, t):
-    _need_dev(name, t, torch.bfloat16)
+# Shape checks run before the device checks.  The library takes the sizes
+# from q and k alone, so a v, out, kv_len or sink that disagrees with them
+# would have the kernels read or write past its end.
+def _shape_is(name, t, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _vec(name, t, n):
+    """An optional contiguous 1-D tensor of n entries (kv_len, sink)."""
+    if t is not None and (tuple(t.shape) != (n,) or (n > 1 and t.stride(0) != 1)):
+        raise ValueError(f"{name} must be a contiguous [{n}] tensor, got shape {tuple(t.shape)}")
+
+
+def _dense_shapes(q, k, v, out, kv_len, sink):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, d]")
+    B, Hq, _, d = q.shape
+    _shape_is("v", v, k.shape)
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in B or d")
+    if out is not None:
+        _shape_is("out", out, q.shape)
+    _vec("kv_len", kv_len, B)
+    _vec("sink", sink, Hq)
+
+
+def _bhsd(name, t, device=None):
+    _need_dev(name, t, torch.bfloat16, device)
     if t.dim() != 4:
         raise ValueError(f"{name} must be [B, H, S, d]")
     if t.stride(3) != 1:
@@ -87,6 +117,8 @@ def workspace_size(B, Hq, Sq, Skv, d, tile_s_kv) -> int:
 
 
 def _workspace(device, nbytes, workspace):
+    if workspace is not None and (workspace.device != device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the query's device")
     if nbytes == 0:
         return workspace
     if workspace is None:
@@ -94,17 +126,23 @@ def _workspace(device, nbytes, workspace):
     return workspace
 
 
+def _dense_devices(q, k, v, out, kv_len, sink):
+    _bhsd("q", q), _bhsd("k", k, q.device), _bhsd("v", v, q.device)
+    if out is not None:
+        _bhsd("out", out, q.device)
+    _need_dev("kv_len", kv_len, torch.int32, q.device)
+    _need_dev("sink", sink, torch.float32, q.device)
+
+
 def prefill(q, k, v, *, kv_len=None, scale=None, sink=None, causal=False, tile_s_kv=0,
             out=None, workspace=None):
     """O = softmax(scale Q K^T + mask [+ sink]) V for dense [B, H, S, d] bf16 tensors."""
-    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
-    _need_dev("kv_len", kv_len, torch.int32)
-    _need_dev("sink", sink, torch.float32)
+    _dense_shapes(q, k, v, out, kv_len, sink)
+    _dense_devices(q, k, v, out, kv_len, sink)
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    _bhsd("out", out)
     nbytes = workspace_size(B, Hq, Sq, Skv, d, tile_s_kv)
     workspace = _workspace(q.device, nbytes, workspace)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -129,9 +167,8 @@ def decode_splitkv(q, k, v, *, kv_len=None, scale=None, sink=None, tile_s_kv=102
     if fused:
         return _decode_fused(q, k, v, kv_len=kv_len, scale=scale, sink=sink,
                              tile_s_kv=tile_s_kv, out=out, workspace=workspace, tickets=tickets)
-    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
-    _need_dev("kv_len", kv_len, torch.int32)
-    _need_dev("sink", sink, torch.float32)
+    _dense_shapes(q, k, v, out, kv_len, sink)
+    _dense_devices(q, k, v, out, kv_len, sink)
     B, Hq, Sq, d = q.shape
     if Sq != 1:
         raise ValueError("decode_splitkv takes one query row per (b, h)")
@@ -151,10 +188,9 @@ def decode_splitkv(q, k, v, *, kv_len=None, scale=None, sink=None, tile_s_kv=102
 
 
 def _decode_fused(q, k, v, *, kv_len, scale, sink, tile_s_kv, out, workspace, tickets):
-    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
-    _need_dev("kv_len", kv_len, torch.int32)
-    _need_dev("sink", sink, torch.float32)
-    _need_dev("tickets", tickets, torch.int32)
+    _dense_shapes(q, k, v, out, kv_len, sink)
+    _dense_devices(q, k, v, out, kv_len, sink)
+    _need_dev("tickets", tickets, torch.int32, q.device)
     B, Hq, Sq, d = q.shape
     if Sq != 1:
         raise ValueError("decode_splitkv takes one query row per (b, h)")
@@ -180,8 +216,8 @@ def _decode_fused(q, k, v, *, kv_len, scale, sink, tile_s_kv, out, workspace, ti
 def splitkv_partial(q, k, v, *, tile_s_kv, kv_len=None, scale=None, causal=False,
                     workspace=None):
     """Partial states only; returns (ml [rows, n_split, 2], ot [rows, n_split, d], workspace)."""
-    _bhsd("q", q), _bhsd("k", k), _bhsd("v", v)
-    _need_dev("kv_len", kv_len, torch.int32)
+    _dense_shapes(q, k, v, None, kv_len, None)
+    _dense_devices(q, k, v, None, kv_len, None)
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     nbytes = workspace_size(B, Hq, Sq, Skv, d, tile_s_kv)
@@ -202,10 +238,17 @@ def splitkv_partial(q, k, v, *, tile_s_kv, kv_len=None, scale=None, causal=False
 
 def splitkv_merge(workspace, *, B, Hq, Sq, d, n_split, sink=None, out=None, device=None):
     """Merge n_split partial states per row from `workspace` into bf16 O [B, Hq, Sq, d]."""
-    _need_dev("sink", sink, torch.float32)
+    if out is not None:
+        _shape_is("out", out, (B, Hq, Sq, d))
+    _vec("sink", sink, Hq)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _need_dev("sink", sink, torch.float32, workspace.device)
     if out is None:
         out = torch.empty((B, Hq, Sq, d), dtype=torch.bfloat16, device=workspace.device)
-    _bhsd("out", out)
+    _bhsd("out", out, workspace.device)
+    if out.dim() != 4 or out.stride(3) != 1:
+        raise ValueError("out must be [B, H, S, d] with a contiguous head dim")
     lib = _lib.load()
     _lib.check(lib.gqa_attention_splitkv_merge(
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
@@ -245,17 +288,36 @@ def paged_append(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, k_new, v
 
 def _paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, k_new, v_new, *, max_q_len,
            scale, sink, causal, page_size, tile_s_kv, out, workspace):
-    _need_dev("q", q, torch.bfloat16)
-    _need_dev("k_cache", k_cache, torch.bfloat16)
-    _need_dev("v_cache", v_cache, torch.bfloat16)
-    _need_dev("cu_seqlens_q", cu_seqlens_q, torch.int32)
-    _need_dev("page_table", page_table, torch.int32)
-    _need_dev("kv_len", kv_len, torch.int32)
-    _need_dev("sink", sink, torch.float32)
-    if q.dim() != 3 or q.stride(2) != 1:
-        raise ValueError("q must be [total_q, Hq, d] with a contiguous head dim")
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [total_q, Hq, d] and the caches [n_pages, page_size, Hkv, d]")
     if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_cache.shape[1] != page_size or k_cache.shape[3] != q.shape[2]:
+        raise ValueError(f"caches {tuple(k_cache.shape)} do not match page_size {page_size} "
+                         f"and q's head dim {q.shape[2]}")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.numel() < 1 or cu_seqlens_q.stride(0) != 1:
+        raise ValueError("cu_seqlens_q must be a contiguous [B + 1] tensor")
+    nseq = cu_seqlens_q.numel() - 1
+    if page_table.dim() != 2 or page_table.shape[0] != nseq:
+        raise ValueError(f"page_table has shape {tuple(page_table.shape)}, expected "
+                         f"[{nseq}, max_pages]")
+    _vec("kv_len", kv_len, nseq)
+    _vec("sink", sink, q.shape[1])
+    if out is not None:
+        _shape_is("out", out, q.shape)
+    dv = q.device
+    _need_dev("q", q, torch.bfloat16)
+    _need_dev("k_cache", k_cache, torch.bfloat16, dv)
+    _need_dev("v_cache", v_cache, torch.bfloat16, dv)
+    _need_dev("cu_seqlens_q", cu_seqlens_q, torch.int32, dv)
+    _need_dev("page_table", page_table, torch.int32, dv)
+    _need_dev("kv_len", kv_len, torch.int32, dv)
+    _need_dev("sink", sink, torch.float32, dv)
+    _need_dev("out", out, torch.bfloat16, dv)
+    if out is not None and out.stride(2) != 1:
+        raise ValueError("out must have a contiguous head dim")
+    if q.stride(2) != 1:
+        raise ValueError("q must be [total_q, Hq, d] with a contiguous head dim")
     if k_cache.dim() != 4 or k_cache.stride(3) != 1:
         raise ValueError("caches must be [n_pages, page_size, Hkv, d] with a contiguous head dim")
     if page_table.dim() != 2 or page_table.stride(1) != 1 or page_table.stride(0) != page_table.shape[1]:
@@ -278,8 +340,8 @@ def _paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, k_new, v_new, 
             d, int(page_size), total_q, int(max_q_len), _scale(scale, d), _ptr(sink),
             int(bool(causal)), int(tile_s_kv), _ptr(workspace), wsb, _stream(q.device)))
         return out
-    _need_dev("k_new", k_new, torch.bfloat16)
-    _need_dev("v_new", v_new, torch.bfloat16)
+    _need_dev("k_new", k_new, torch.bfloat16, dv)
+    _need_dev("v_new", v_new, torch.bfloat16, dv)
     if k_new is None or v_new is None or k_new.shape != (total_q, Hkv, d) or \
             v_new.shape != k_new.shape or k_new.stride() != v_new.stride() or k_new.stride(2) != 1:
         raise ValueError("k_new and v_new must both be [total_q, Hkv, d] with equal strides "

@@ -13,6 +13,8 @@ Family A: short groups (4 or 32 rows; two q-tiles at d = 256) over
 B x Hkv = 256, one pass and one split of 64 keys, dense and paged.
 Family B: 128-, 256- and 512-row groups over B x Hkv = 288, at d = 64 and
 128, one pass and splits of 64 keys, dense and paged, causal.
+Head-major pools: a paged cache stored [n_pages, Hkv, 64, d] and passed by
+strides gives the token-major pool's result bit for bit.
 """
 
 import numpy as np
@@ -111,3 +113,37 @@ def test_paged_64_row_groups(d, tile):
 @pytest.mark.parametrize("Sq", [1, 8])
 def test_paged_split_stream_wide_grid(d, Sq):
     run_case("paged", 32, 4, 4, Sq, 128, d, 64, Sq > 1, seed=500 + d + Sq)
+
+
+# The pool stored head-major ([n_pages, Hkv, 64, d]) and passed through the
+# stride arguments as the same logical [n_pages, 64, Hkv, d] view: the
+# result must match the oracle and, bit for bit, the token-major pool's.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Sq", [1, 8])
+@pytest.mark.parametrize("tile", [0, 64])
+def test_paged_head_major_pool(d, Sq, tile):
+    B, Hkv, G = 6, 2, 4
+    print(f"[case] head-major pool d={d} Sq={Sq} tile={tile}", flush=True)
+    m = gqa()
+    r = np.random.default_rng(600 + d + Sq + tile)
+    q_lens = [int(x) for x in r.integers(1, Sq + 1, B)]
+    kv_lens = [max(q, int(x)) for q, x in zip(q_lens, r.integers(1, 300, B))]
+    w = workloads.make_paged(B=B, Hq=Hkv * G, Hkv=Hkv, d=d, q_lens=q_lens, kv_lens=kv_lens,
+                             seed=600 + d)
+    g = to_dev(w)
+    kh = g["k_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vh = g["v_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert kh.stride(1) == d and kh.stride(2) == 64 * d
+    outs = []
+    for kc, vc in ((g["k_cache"], g["v_cache"]), (kh, vh)):
+        outs.append(m.paged(g["q"], g["cu_seqlens_q"], kc, vc, g["page_table"], g["kv_len"],
+                            max_q_len=w["max_q_len"], scale=w["scale"], sink=g["sink"],
+                            causal=Sq > 1, tile_s_kv=tile))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    want = oracle.paged_attention_fp64(to_f64(w["q"]), w["cu_seqlens_q"].numpy(),
+                                       to_f64(w["k_cache"]), to_f64(w["v_cache"]),
+                                       w["page_table"].numpy(), w["kv_len"].numpy(),
+                                       scale=w["scale"], page_size=64, sink=to_f64(w["sink"]),
+                                       causal=Sq > 1)
+    check(outs[1].float().cpu().numpy(), want, f"head-major pool d={d} Sq={Sq} tile={tile}")

@@ -181,11 +181,14 @@ gqa::AttnArgs dense_args(const void* q, const int64_t* qs, const void* k, const 
 }
 
 // Shared checks of the dense entry points.
-// K/V tiles are read through buffer resources with 32-bit offsets spanning
-// 32 key rows; this bound keeps every offset in range.
+// K/V tiles are read through buffer resources whose per-lane offsets and
+// size are 32-bit byte counts spanning up to 63 key rows past the tile's
+// first (the prefill kernel's 64-key tiles): 63 * stride * 2 + 512 bytes
+// stays below 2^32 for every stride below 2^25 elements.
+constexpr int64_t kMaxKeyStride = (int64_t)1 << 25;
 gqa_status_t check_key_stride(const char* name, int64_t st) {
-  if (st >= (int64_t)1 << 26)
-    return fail(GQA_ERR_UNSUPPORTED, "%s key-row stride (%lld) must be below 2^26 elements", name,
+  if (st >= kMaxKeyStride)
+    return fail(GQA_ERR_UNSUPPORTED, "%s key-row stride (%lld) must be below 2^25 elements", name,
                 (long long)st);
   return GQA_OK;
 }

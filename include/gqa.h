@@ -49,7 +49,9 @@
  *  - Base pointers must be 16-byte aligned and the (b, h, s) strides of
  *    bf16 tensors multiples of 8 elements, else GQA_ERR_UNSUPPORTED.  The
  *    stride between consecutive key rows of K and V (dense s stride, paged
- *    kv_stride_row) must be below 2^26 elements, else GQA_ERR_UNSUPPORTED.
+ *    kv_stride_row, the append form's new_stride_t) must be below 2^25
+ *    elements, else GQA_ERR_UNSUPPORTED: a 64-key tile is addressed with
+ *    32-bit byte offsets from its first row.
  *    d must be 32, 64, 128 or 256, else GQA_ERR_UNSUPPORTED (the AstrAI
  *    commit log's kernels cover prefill at head dim 32 and decode at 256
  *    besides 64 and 128).  A launch whose grid would exceed 2^32 - 1
@@ -256,7 +258,7 @@ gqa_status_t gqa_attention_paged(const void* q, int64_t q_stride_t, int64_t q_st
  *
  *  k_new / v_new : bf16 [total_q, Hkv, d] packed like q, strides (t, h) in
  *                 elements (new_stride_t, new_stride_h; d contiguous; the
- *                 same strides for both; new_stride_t below 2^26).  Token i of sequence b (row
+ *                 same strides for both; new_stride_t below 2^25).  Token i of sequence b (row
  *                 cu_seqlens_q[b] + i) holds key row j = kv_len[b] - q_len_b
  *                 + i of that sequence: kv_len counts the new tokens, and
  *                 kv_len[b] >= q_len_b (tokens that would land before key

@@ -42,17 +42,41 @@ int main(void) {
   expect("stride not x8", PREFILL(P, bad, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
   expect("NULL strides", PREFILL(P, NULL, 64, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
   {
+    /* Key-row strides: a 64-key tile spans 63 rows of 32-bit byte offsets
+     * from its first row, so the bound is 2^25 elements.  Just below it the
+     * stride check passes and the call stops at the (missing) workspace;
+     * at the bound and above it is refused. */
+    const int64_t big = ((int64_t)1 << 25) - 8;
+    const int64_t at[3] = {(int64_t)1 << 40, (int64_t)1 << 34, (int64_t)1 << 25};
+    const int64_t below[3] = {(int64_t)1 << 40, (int64_t)1 << 34, big};
     const int64_t huge[3] = {(int64_t)1 << 40, (int64_t)1 << 34, (int64_t)1 << 26};
     expect("k row stride 2^26",
            gqa_attention_prefill(P, s, P, huge, P, s, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
                                  NULL, 0, 0, NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
-    expect("v row stride 2^26",
-           gqa_attention_prefill(P, s, P, s, P, huge, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
-                                 NULL, 0, 0, NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+    expect("k row stride 2^25",
+           gqa_attention_prefill(P, s, P, at, P, s, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
+                                 NULL, 0, 64, NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+    expect("k row stride 2^25 - 8 passes (stops at the workspace)",
+           gqa_attention_prefill(P, s, P, below, P, s, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
+                                 NULL, 0, 64, NULL, 0, NULL), GQA_ERR_WORKSPACE);
+    expect("v row stride 2^25",
+           gqa_attention_prefill(P, s, P, s, P, at, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
+                                 NULL, 0, 64, NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+    expect("v row stride 2^25 - 8 passes (stops at the workspace)",
+           gqa_attention_prefill(P, s, P, s, P, below, P, s, 1, 4, 1, 16, 128, 64, NULL, 0.125f,
+                                 NULL, 0, 64, NULL, 0, NULL), GQA_ERR_WORKSPACE);
     expect("paged row stride 2^26",
            gqa_attention_paged(P, 4096, 128, P, P, P, (int64_t)1 << 33, (int64_t)1 << 26, 128, P,
                                64, P, P, 4096, 128, 8, 32, 1, 128, 64, 100, 64, 0.088f, NULL, 0, 0,
                                NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+    expect("paged row stride 2^25",
+           gqa_attention_paged(P, 4096, 128, P, P, P, (int64_t)1 << 33, (int64_t)1 << 25, 128, P,
+                               64, P, P, 4096, 128, 8, 32, 1, 128, 64, 100, 64, 0.088f, NULL, 0,
+                               512, NULL, 0, NULL), GQA_ERR_UNSUPPORTED);
+    expect("paged row stride 2^25 - 8 passes (stops at the workspace)",
+           gqa_attention_paged(P, 4096, 128, P, P, P, (int64_t)1 << 33, big, 128, P, 64, P, P,
+                               4096, 128, 8, 32, 1, 128, 64, 100, 64, 0.088f, NULL, 0, 512, NULL,
+                               0, NULL), GQA_ERR_WORKSPACE);
   }
   expect("d = 96", PREFILL(P, s, 96, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
   expect("Hq % Hkv", PREFILL(P, s, 64, 6, 4, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
@@ -116,6 +140,12 @@ int main(void) {
   expect("append new stride 1020", APPEND(P, P, 1020, 1), GQA_ERR_UNSUPPORTED);
   expect("append 36 rows per kv head", APPEND(P, P, 1024, 9), GQA_ERR_UNSUPPORTED);
   expect("append new stride 2^26", APPEND(P, P, (int64_t)1 << 26, 1), GQA_ERR_UNSUPPORTED);
+  expect("append new stride 2^25", APPEND(P, P, (int64_t)1 << 25, 1), GQA_ERR_UNSUPPORTED);
+  expect("append new stride 2^25 - 8 passes (stops at the workspace)",
+         gqa_attention_paged_append(P, 4096, 128, P, P, P, 8192, 128, 128, P, 64, P, P, P,
+                                    ((int64_t)1 << 25) - 8, 128, P, 4096, 128, 8, 32, 8, 128, 64,
+                                    8, 1, 0.088f, NULL, 0, 512, NULL, 0, NULL),
+         GQA_ERR_WORKSPACE);
   expect("append empty batch",
          gqa_attention_paged_append(NULL, 0, 0, NULL, NULL, NULL, 0, 0, 0, NULL, 0, NULL, NULL,
                                     NULL, 0, 0, NULL, 0, 0, 0, 32, 8, 128, 64, 0, 0, 0.088f, NULL,

@@ -126,24 +126,31 @@ def attention_fp64(q, k, v, *, scale: float, kv_len=None, sink=None,
 
 
 def attention_rows_fp64(q, k, v, b_idx, h_idx, i_idx, *, scale: float, kv_len=None,
-                        sink=None, causal: bool = False) -> np.ndarray:
+                        sink=None, causal: bool = False, row_chunk: int = 512) -> np.ndarray:
     """The same definition evaluated only at selected rows (b, h, i).
 
-    Used to check full-size runs on sampled outputs; returns [len(b_idx), d].
+    Used to check full-size runs on selected outputs; returns [len(b_idx), d].
+    The rows asked for one (b, h) are evaluated together (each still over
+    its own visible keys), in groups of at most `row_chunk`.
     """
     q = np.asarray(q)
     B, Hq, Sq, d = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
     G = Hq // Hkv
     kvl = np.full(B, Skv, dtype=np.int64) if kv_len is None else np.asarray(kv_len, dtype=np.int64)
+    b_idx, h_idx, i_idx = (np.asarray(x, dtype=np.int64) for x in (b_idx, h_idx, i_idx))
     out = np.zeros((len(b_idx), d), dtype=np.float64)
-    for t, (b, h, i) in enumerate(zip(b_idx, h_idx, i_idx)):
+    for b, h in sorted(set(zip(b_idx.tolist(), h_idx.tolist()))):
+        sel = np.nonzero((b_idx == b) & (h_idx == h))[0]
         n = int(min(max(kvl[b], 0), Skv))
-        hi = _visible(n, Sq, np.array([i]), causal)
-        K = _f64(k[b, h // G, :int(hi[0])])
-        V = _f64(v[b, h // G, :int(hi[0])])
-        out[t] = _attend_rows(_f64(q[b, h, i])[None, :], K, V, hi, scale,
-                              None if sink is None else float(np.asarray(sink)[h]))[0]
+        for c0 in range(0, sel.size, row_chunk):
+            part = sel[c0:c0 + row_chunk]
+            hi = _visible(n, Sq, i_idx[part], causal)
+            kmax = int(hi.max())
+            K = _f64(k[b, h // G, :kmax])
+            V = _f64(v[b, h // G, :kmax])
+            out[part] = _attend_rows(_f64(q[b, h, i_idx[part]]), K, V, hi, scale,
+                                     None if sink is None else float(np.asarray(sink)[h]))
     return out
 
 

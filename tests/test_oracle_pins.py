@@ -173,6 +173,86 @@ def test_weights_sum_to_one():
             assert np.all(w[1, :, :, 9:] == 0.0)
 
 
+def _scores_with_sink(q, k, scale, kv_len, sink, causal):
+    """Scores of every row with the sink appended as one more column, invisible
+    keys at -inf, written with einsum (not the oracle's matmul).  Returns
+    [B, Hq, Sq, Skv + 1] and the number of visible keys per row."""
+    B, Hq, Sq, d = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    kx = np.stack([k[:, h // G] for h in range(Hq)], axis=1)      # [B, Hq, Skv, d]
+    s = scale * np.einsum("bhid,bhjd->bhij", q, kx)
+    hi = np.empty((B, Sq), dtype=np.int64)
+    for b in range(B):
+        for i in range(Sq):
+            hi[b, i] = kv_len[b] if not causal else min(max(kv_len[b] - Sq + i + 1, 0), kv_len[b])
+    vis = np.arange(Skv)[None, None, None, :] < hi[:, None, :, None]
+    s = np.where(vis, s, -np.inf)
+    sk = np.broadcast_to((np.full(Hq, -np.inf) if sink is None else sink)[None, :, None, None],
+                         (B, Hq, Sq, 1))
+    return np.concatenate([s, sk], axis=-1), hi
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_definition_weights_are_a_softmax_summing_to_one(causal, with_sink):
+    """The weights inside attention_fp64 itself (the function every GPU
+    comparison uses): with V the identity (one key per d column), O[.., j] is
+    the weight of key j.  They must equal scipy's softmax over the row's
+    scores with the sink appended as one more column (the sink column has no
+    value row, so its weight is 1 - sum_j O[.., j]), be zero past the row's
+    visible keys, and -- with V all ones -- every row must sum to 1 minus the
+    sink weight (to 1 exactly up to rounding without a sink).  Groups of 4
+    over 3 kv heads, so a wrong head map changes the weights."""
+    from scipy.special import softmax
+    B, Hkv, G, Sq, d = 2, 3, 4, 6, 24
+    Skv = d                                    # V = identity: key j carries e_j
+    Hq = Hkv * G
+    q, k = rand(B, Hq, Sq, d), rand(B, Hkv, Skv, d)
+    sink = rand(Hq) if with_sink else None
+    kv_len = [24, 10]
+    eye = np.broadcast_to(np.eye(Skv), (B, Hkv, Skv, d)).copy()
+    w = oracle.attention_fp64(q, k, eye, scale=0.35, kv_len=kv_len, sink=sink, causal=causal)
+    s_ext, hi = _scores_with_sink(q, k, 0.35, kv_len, sink, causal)
+    live = np.isfinite(s_ext).any(-1)
+    want = np.zeros_like(s_ext)
+    want[live] = softmax(s_ext[live], axis=-1)
+    np.testing.assert_allclose(w, want[..., :Skv], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(w.sum(-1)[live] + want[..., Skv][live], 1.0, rtol=0, atol=1e-14)
+    for b in range(B):
+        for i in range(Sq):
+            assert np.all(w[b, :, i, hi[b, i]:] == 0.0)
+    ones = oracle.attention_fp64(q, k, np.ones((B, Hkv, Skv, d)), scale=0.35, kv_len=kv_len,
+                                 sink=sink, causal=causal)
+    tot = np.where(live[..., None], 1.0 - want[..., Skv][..., None], 0.0)
+    np.testing.assert_allclose(ones, np.broadcast_to(tot, ones.shape), rtol=0, atol=1e-14)
+    if not with_sink:
+        assert np.all(np.abs(ones[live] - 1.0) <= 1e-15)
+
+
+def test_softmax_weights_head_map_matches_the_definition():
+    """softmax_weights_fp64 (used to size the rounding bound of the GPU tests)
+    gives the same weights as attention_fp64 with V = identity at G = 4 over 3
+    kv heads, and a head map of h % Hkv instead of h // G would not."""
+    B, Hkv, G, Sq, d = 2, 3, 4, 5, 16
+    Skv, Hq = d, Hkv * G
+    q, k = rand(B, Hq, Sq, d), rand(B, Hkv, Skv, d)
+    sink = rand(Hq)
+    eye = np.broadcast_to(np.eye(Skv), (B, Hkv, Skv, d)).copy()
+    for causal in (False, True):
+        w_def = oracle.attention_fp64(q, k, eye, scale=0.3, kv_len=[16, 7], sink=sink,
+                                      causal=causal)
+        w, ws = oracle.softmax_weights_fp64(q, k, scale=0.3, kv_len=[16, 7], sink=sink,
+                                            causal=causal)
+        np.testing.assert_allclose(w, w_def, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(ws, 1.0 - w_def.sum(-1), rtol=0, atol=1e-14)
+        # the slip this guards against: query head h reading kv head h % Hkv
+        k_slip = np.stack([k[:, (h % Hkv)] for h in range(Hq)], axis=1)
+        w_slip = oracle.attention_fp64(q, k_slip, np.broadcast_to(np.eye(Skv), (B, Hq, Skv, d)).copy(),
+                                       scale=0.3, kv_len=[16, 7], sink=sink, causal=causal)
+        assert np.abs(w_slip - w).max() > 1e-2
+
+
 def test_gqa_equals_repeated_mha():
     B, Hkv, G, Sq, Skv, d = 2, 3, 4, 5, 17, 8
     q, k, v = rand(B, Hkv * G, Sq, d), rand(B, Hkv, Skv, d), rand(B, Hkv, Skv, d)
@@ -413,10 +493,11 @@ def test_row_subsets_match_full():
     q, k, v = rand(2, 4, 6, 8), rand(2, 2, 12, 8), rand(2, 2, 12, 8)
     sink = rand(4)
     full = oracle.attention_fp64(q, k, v, scale=0.3, kv_len=[12, 5], sink=sink, causal=True)
-    bi, hi, ii = [0, 1, 1, 0], [3, 0, 2, 1], [5, 0, 4, 2]
-    rows = oracle.attention_rows_fp64(q, k, v, bi, hi, ii, scale=0.3, kv_len=[12, 5], sink=sink,
-                                      causal=True)
-    np.testing.assert_allclose(rows, full[bi, hi, ii], rtol=1e-13, atol=1e-15)
+    bi, hi, ii = [0, 1, 1, 0, 1, 1, 0], [3, 0, 2, 1, 0, 0, 3], [5, 0, 4, 2, 3, 1, 0]
+    for chunk in (512, 1):  # rows of one (b, h) together, and one at a time
+        rows = oracle.attention_rows_fp64(q, k, v, bi, hi, ii, scale=0.3, kv_len=[12, 5],
+                                          sink=sink, causal=True, row_chunk=chunk)
+        np.testing.assert_allclose(rows, full[bi, hi, ii], rtol=1e-13, atol=1e-15)
     w = workloads.make_paged(B=3, Hq=4, Hkv=1, d=8, max_q=6, max_kv=150, seed=5, extra_pages=1)
     f = workloads.to_f64
     args = dict(scale=w["scale"], page_size=64, sink=f(w["sink"]))

@@ -1,22 +1,32 @@
-"""The parity bound shared by the GPU tests whose inputs give rows that see
-only a few keys.
+"""The parity bound of the GPU tests, with the one exception the method's
+rounding forces, derived per element and counted.
 
-The bar is max-abs <= 1e-2 and mean-abs <= 1e-3 against the fp64 oracle,
-with one derived exception: an output whose exact value has |O| >= 2 may be
-off by one bf16 spacing of that value (2^-6 on [2, 4)).  Two roundings that
-the method makes set that bound.  P is rounded to bf16 before P.V, which
-re-weights the visible V rows by up to 2^-9 relative, so O moves by up to
-2^-9 * max|v - O| before its own rounding.  O is then rounded to bf16, which
-adds up to half a spacing.  On a row that sees only a few keys, with |O| in
-[2, 4), the sum can pass 1e-2 (a 2-key row with |v - O| ~ 3 gives about
-0.006 + 0.0078).  Below |O| = 2 one spacing is under 1e-2 and the usual bar
-holds unchanged.
+The bar is max-abs <= 1e-2 and mean-abs <= 1e-3 against the fp64 oracle.
+The kernels round each softmax weight P_j to bf16 before P.V and take the row
+sum over the same rounded weights (so the weights still sum to one), then
+round O to bf16 once.  Write the exact weights w_j (the sink a column whose
+value row is 0 and whose weight is not rounded) and the rounded ones
+w~_j = w_j (1 + d_j) / (1 + sum_i w_i d_i), |d_j| <= u = 2^-8, the unit
+roundoff of an 8-significant-bit format.  Because sum_j w_j (v_j - O) = 0,
+
+    O~ - O = sum_j (w~_j - w_j)(v_j - O) = sum_j w_j d_j (v_j - O) / (1 + dbar),
+
+so |O~ - O| <= u / (1 - u) * sum_j w_j |v_j - O|   (per output element), and
+the bf16 store adds at most half a spacing of the value it rounds.  fp32
+accumulation, the exp2 instruction and the merge add errors of order 2^-22
+relative, covered by a 1e-6 slack.  Rows that see many keys average the d_j
+out and stay far below 1e-2; a row that sees a few keys whose values lie far
+from O can exceed it.  Such an element passes only if it stays within this
+derived bound, and every one of them is printed and counted.
 """
 
 import numpy as np
 
+import oracle
+
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
+U_BF16 = 2.0 ** -8
 
 
 def bf16_spacing(x):
@@ -26,16 +36,83 @@ def bf16_spacing(x):
     return np.where(a > 0, np.exp2(e - 7), 0.0)
 
 
-def check(got, want, what):
+def rounding_bound(o_exact, spread):
+    """Largest error the two bf16 roundings can cause at an element whose
+    exact value is o_exact and whose sum_j w_j |v_j - O| is `spread`."""
+    wt = U_BF16 / (1.0 - U_BF16) * np.asarray(spread, dtype=np.float64)
+    return wt + 0.5 * bf16_spacing(np.abs(o_exact) + wt) + 1e-6
+
+
+def spread_dense(q, k, v, *, scale, kv_len, sink, causal, want, idx):
+    """sum_j w_j |v_j - O| at the elements idx = (b, h, i, e) of a dense
+    problem, from the oracle's weights (softmax_weights_fp64, which is pinned
+    to the definition); inputs are fp64 arrays."""
+    B, Hq, Sq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros(len(idx[0]))
+    rows = {}
+    for t, (b, h, i, e) in enumerate(zip(*idx)):
+        key = (int(b), int(h))
+        if key not in rows:
+            snk = None if sink is None else np.asarray([sink[h]])
+            kl = None if kv_len is None else [int(kv_len[b])]
+            w, _ = oracle.softmax_weights_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1],
+                                               scale=scale, kv_len=kl, sink=snk, causal=causal)
+            rows[key] = w[0, 0]
+        w = rows[key][i]
+        vis = w > 0
+        vj = v[b, h // G, :, e][vis]
+        out[t] = float(np.sum(w[vis] * np.abs(vj - want[b, h, i, e])))
+    return out
+
+
+def spread_paged(w_inp, *, causal, want, idx):
+    """The same for a paged problem (packed rows t, heads h, elements e): the
+    sequence's K/V are gathered from the pool and treated as dense."""
+    from workloads import to_f64
+    cu = w_inp["cu_seqlens_q"].numpy().astype(np.int64)
+    kl = w_inp["kv_len"].numpy().astype(np.int64)
+    q = to_f64(w_inp["q"])
+    Ks = oracle.gather_paged_fp64(to_f64(w_inp["k_cache"]), w_inp["page_table"].numpy(), kl, 64)
+    Vs = oracle.gather_paged_fp64(to_f64(w_inp["v_cache"]), w_inp["page_table"].numpy(), kl, 64)
+    sink = None if w_inp["sink"] is None else to_f64(w_inp["sink"])
+    Hq = q.shape[1]
+    G = Hq // Ks[0].shape[0]
+    out = np.zeros(len(idx[0]))
+    for n, (t, h, e) in enumerate(zip(*idx)):
+        b = int(np.searchsorted(cu, t, side="right") - 1)
+        qs = q[cu[b]:cu[b + 1], h][None, None]                       # [1, 1, q_len, d]
+        kb = Ks[b][h // G][None, None]
+        snk = None if sink is None else np.asarray([sink[h]])
+        w, _ = oracle.softmax_weights_fp64(qs, kb, scale=w_inp["scale"], kv_len=[kl[b]],
+                                           sink=snk, causal=causal)
+        wr = w[0, 0, t - cu[b]]
+        vis = wr > 0
+        out[n] = float(np.sum(wr[vis] * np.abs(Vs[b][h // G][:, e][vis] - want[t, h, e])))
+    return out
+
+
+def check(got, want, what, spread_at=None):
+    """Assert the bar.  Elements above 1e-2 must stay within the derived
+    rounding bound (spread_at(idx) gives their sum_j w_j |v_j - O|); they are
+    counted and printed."""
     got = np.asarray(got, dtype=np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - want)
-    bound = np.maximum(MAX_ABS, np.where(np.abs(want) >= 2.0, bf16_spacing(want), 0.0))
     mean = float(err.mean()) if err.size else 0.0
-    over = int((err > MAX_ABS).sum())
-    worst = float((err / bound).max(initial=0.0))
-    print(f"  {what}: max_abs={err.max(initial=0):.3e} mean_abs={mean:.3e} "
-          f"above 1e-2: {over} (worst {worst:.2f} of the bound)", flush=True)
+    over = err > MAX_ABS
+    n_over = int(over.sum())
+    msg = (f"  {what}: max_abs={err.max(initial=0):.3e} mean_abs={mean:.3e} "
+           f"exempt (above 1e-2, within the rounding bound): {n_over}")
+    if n_over:
+        assert spread_at is not None, f"{what}: {n_over} elements above 1e-2"
+        idx = np.nonzero(over)
+        bound = rounding_bound(want[idx], spread_at(idx))
+        for j in range(n_over):
+            print(f"    exempt element {tuple(int(x[j]) for x in idx)}: err {err[idx][j]:.4e} "
+                  f"|O| {abs(want[idx][j]):.4f} bound {bound[j]:.4e}", flush=True)
+        assert np.all(err[idx] <= bound), f"{what}: above the rounding bound"
+    print(msg, flush=True)
     assert mean <= MEAN_ABS, f"{what}: mean {mean}"
-    assert np.all(err <= bound), f"{what}: max {err.max()} at {np.argmax(err)}"

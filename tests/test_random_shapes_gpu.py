@@ -2,8 +2,9 @@
 size, causal flag and split size in combinations the named cases do not list.
 
 Each case is drawn from a fixed-seed generator and checked in full against the
-fp64 oracle, to the bound in bf16_bound.py (the usual bar, and one bf16
-spacing where |O| >= 2).
+fp64 oracle, to the bound in bf16_bound.py: the usual bar, where an element
+above 1e-2 must stay within the rounding bound derived there from the oracle's
+weights (each such element is printed and counted).
 """
 
 import random
@@ -14,7 +15,8 @@ import torch
 
 import oracle
 import workloads
-from bf16_bound import bf16_spacing, check
+import bf16_bound
+from bf16_bound import check
 from workloads import to_f64
 
 
@@ -57,11 +59,15 @@ def _dense_case(r, seed):
     else:
         out = gqa().prefill(g["q"], g["k"], g["v"], causal=causal, tile_s_kv=tile, **kw)
     torch.cuda.synchronize()
-    want = oracle.attention_fp64(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]),
-                                 scale=inp["scale"], kv_len=inp["kv_len"].numpy(),
-                                 sink=None if inp["sink"] is None else to_f64(inp["sink"]),
+    q64, k64, v64 = to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"])
+    snk = None if inp["sink"] is None else to_f64(inp["sink"])
+    kvl = inp["kv_len"].numpy()
+    want = oracle.attention_fp64(q64, k64, v64, scale=inp["scale"], kv_len=kvl, sink=snk,
                                  causal=causal)
-    check(out.float().cpu().numpy(), want, what)
+    spread = lambda idx: bf16_bound.spread_dense(q64, k64, v64, scale=inp["scale"],  # noqa: E731
+                                                 kv_len=kvl, sink=snk, causal=causal,
+                                                 want=want, idx=idx)
+    check(out.float().cpu().numpy(), want, what, spread)
 
 
 def _paged_case(r, seed):
@@ -99,15 +105,84 @@ def _paged_case(r, seed):
                                        w["page_table"].numpy(), w["kv_len"].numpy(),
                                        scale=w["scale"], page_size=64, sink=to_f64(w["sink"]),
                                        causal=causal)
-    check(out.float().cpu().numpy(), want, what)
+    # (with append, w's pools already hold the new rows: the attention's keys)
+    spread = lambda idx: bf16_bound.spread_paged(w, causal=causal, want=want, idx=idx)  # noqa: E731
+    check(out.float().cpu().numpy(), want, what, spread)
     if append:
         assert torch.equal(kc.cpu().view(torch.int16), w["k_cache"].view(torch.int16))
         assert torch.equal(vc.cpu().view(torch.int16), w["v_cache"].view(torch.int16))
 
 
-def test_bound_is_one_spacing_only_above_two():
-    assert bf16_spacing(1.99) == 2.0 ** -7 and bf16_spacing(2.0) == 2.0 ** -6
-    assert bf16_spacing(-3.5) == 2.0 ** -6 and bf16_spacing(0.0) == 0.0
+def test_spacing():
+    sp = bf16_bound.bf16_spacing
+    assert sp(1.99) == 2.0 ** -7 and sp(2.0) == 2.0 ** -6
+    assert sp(-3.5) == 2.0 ** -6 and sp(0.0) == 0.0 and sp(0.75) == 2.0 ** -8
+
+
+def test_rounding_bound_covers_simulated_rounding():
+    """CPU check of the derivation: rows of 1-6 keys with values spread far
+    from O, weights rounded to bf16 (RNE, through torch), normalised by the
+    sum of the rounded weights, O rounded to bf16.  Every error stays within
+    rounding_bound, some exceed 1e-2 (so the exception is needed), and the
+    bound is not loose by more than a small factor on the worst rows."""
+    rng = np.random.default_rng(0)
+    worst, above = 0.0, 0
+    for _ in range(4000):
+        n = int(rng.integers(1, 7))
+        s = rng.normal(0.0, 2.0, n)
+        v = rng.normal(0.0, 3.0, n)
+        sink = rng.normal() if rng.random() < 0.5 else -np.inf
+        m = max(s.max(), sink)
+        off = rng.uniform(0, 8)  # the kernels' reference may lag the max by up to 8 (log2)
+        p = np.exp2((s - m) * 1.4426950408889634 + off)
+        ps = np.exp2((sink - m) * 1.4426950408889634 + off) if sink > -np.inf else 0.0
+        w = p / (p.sum() + ps)
+        o = float(np.sum(w * v))
+        pr = torch.tensor(p, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+        ot = np.sum(pr * v) / (pr.sum() + ps)
+        ob = float(torch.tensor(ot, dtype=torch.float32).to(torch.bfloat16).double())
+        err = abs(ob - o)
+        bound = float(bf16_bound.rounding_bound(o, np.sum(w * np.abs(v - o))))
+        assert err <= bound, (err, bound, n)
+        above += err > bf16_bound.MAX_ABS
+        worst = max(worst, err / bound)
+    assert above > 0 and worst > 0.4
+
+
+def test_spread_helpers():
+    """sum_j w_j |v_j - O| from the helpers equals the sum written out from
+    the softmax of the scores (two keys plus a sink), and the paged helper
+    agrees with the dense one on the same sequence."""
+    from scipy.special import softmax
+    w = workloads.make_paged(B=2, Hq=4, Hkv=2, d=8, q_lens=[2, 3], kv_lens=[2, 70], seed=3)
+    q, sink = to_f64(w["q"]), to_f64(w["sink"])
+    ks = oracle.gather_paged_fp64(to_f64(w["k_cache"]), w["page_table"].numpy(),
+                                  w["kv_len"].numpy(), 64)
+    vs = oracle.gather_paged_fp64(to_f64(w["v_cache"]), w["page_table"].numpy(),
+                                  w["kv_len"].numpy(), 64)
+    want = oracle.paged_attention_fp64(q, w["cu_seqlens_q"].numpy(), to_f64(w["k_cache"]),
+                                       to_f64(w["v_cache"]), w["page_table"].numpy(),
+                                       w["kv_len"].numpy(), scale=w["scale"], page_size=64,
+                                       sink=sink, causal=True)
+    # sequence 0: 2 queries over 2 keys (bottom-right causal: row 0 sees key 0)
+    t, h, e = 1, 3, 5
+    s_ = w["scale"] * ks[0][h // 2] @ q[t, h]
+    p_ = softmax(np.append(s_, sink[h]))
+    direct = float(np.sum(p_[:2] * np.abs(vs[0][h // 2][:, e] - want[t, h, e])))
+    got = bf16_bound.spread_paged(w, causal=True, want=want, idx=(np.array([t]), np.array([h]),
+                                                                   np.array([e])))
+    assert abs(got[0] - direct) <= 1e-12
+    # sequence 1 through the dense helper: its rows as a [1, Hq, 3, d] problem
+    qd = q[2:5].transpose(1, 0, 2)[None]
+    kd = np.stack(ks[1])[None]
+    vd = np.stack(vs[1])[None]
+    wd = oracle.attention_fp64(qd, kd, vd, scale=w["scale"], sink=sink, causal=True)
+    idx_d = (np.array([0, 0]), np.array([0, 3]), np.array([2, 1]), np.array([7, 0]))
+    dense = bf16_bound.spread_dense(qd, kd, vd, scale=w["scale"], kv_len=[70], sink=sink,
+                                    causal=True, want=wd, idx=idx_d)
+    paged = bf16_bound.spread_paged(w, causal=True, want=want,
+                                    idx=(np.array([4, 3]), np.array([0, 3]), np.array([7, 0])))
+    np.testing.assert_allclose(dense, paged, rtol=1e-12)
 
 
 @pytest.mark.gpu

@@ -7,6 +7,7 @@ eager fallback: without the built library every call raises.
 
     prefill(q, k, v, ...)          dense [B, H, S, d] tensors, one pass or split-KV
     decode_splitkv(q, k, v, ...)   Sq = 1, split-KV partials + merge kernel
+    decode_splitkv_noalloc(...)    the same with the library's own scratch (allocates nothing)
     splitkv_partial / splitkv_merge  the two split-KV phases on their own
     paged(q, cu_seqlens_q, k_cache, v_cache, page_table, kv_len, ...)
     workspace_size(...)
@@ -24,7 +25,7 @@ from . import _lib
 from ._lib import (GQAError, GQAInvalidArgument, GQAUnsupported,  # noqa: F401
                    GQAWorkspaceError)
 
-__all__ = ["prefill", "decode_splitkv", "splitkv_partial", "splitkv_merge", "paged",
+__all__ = ["prefill", "decode_splitkv", "decode_splitkv_noalloc", "splitkv_partial", "splitkv_merge", "paged",
            "paged_append", "workspace_size", "n_splits", "GQAError"]
 
 
@@ -184,6 +185,27 @@ def decode_splitkv(q, k, v, *, kv_len=None, scale=None, sink=None, tile_s_kv=102
         _ptr(v), _lib.strides3(v.stride()[:3]), _ptr(out), _lib.strides3(out.stride()[:3]),
         B, Hq, Hkv, Skv, d, _ptr(kv_len), _scale(scale, d), _ptr(sink), int(tile_s_kv),
         _ptr(workspace), wsb, _stream(q.device)))
+    return out
+
+
+def decode_splitkv_noalloc(q, k, v, *, kv_len=None, scale=None, sink=None, tile_s_kv=1024,
+                           out):
+    """decode_splitkv without a workspace: the library keeps the partial
+    states in a fixed scratch buffer of its own (one per GPU), so the call
+    allocates nothing; `out` is required.  Calls that overlap in time on one
+    GPU share that buffer and race."""
+    _dense_shapes(q, k, v, out, kv_len, sink)
+    _dense_devices(q, k, v, out, kv_len, sink)
+    B, Hq, Sq, d = q.shape
+    if Sq != 1:
+        raise ValueError("decode_splitkv_noalloc takes one query row per (b, h)")
+    Hkv, Skv = k.shape[1], k.shape[2]
+    lib = _lib.load()
+    _lib.check(lib.gqa_attention_decode_splitkv_noalloc(
+        _ptr(q), _lib.strides3(q.stride()[:3]), _ptr(k), _lib.strides3(k.stride()[:3]),
+        _ptr(v), _lib.strides3(v.stride()[:3]), _ptr(out), _lib.strides3(out.stride()[:3]),
+        B, Hq, Hkv, Skv, d, _ptr(kv_len), _scale(scale, d), _ptr(sink), int(tile_s_kv),
+        _stream(q.device)))
     return out
 
 

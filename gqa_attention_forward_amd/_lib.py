@@ -19,6 +19,7 @@ GQA_ERR_INVALID_ARGUMENT = 1
 GQA_ERR_UNSUPPORTED = 2
 GQA_ERR_WORKSPACE = 3
 GQA_ERR_HIP = 4
+NOALLOC_SCRATCH_BYTES = 8 << 20  # GQA_NOALLOC_SCRATCH_BYTES
 
 
 class GQAError(RuntimeError):
@@ -68,6 +69,8 @@ SIGNATURES = {
     "gqa_attention_decode_splitkv_fused": [_P, _STR3, _P, _STR3, _P, _STR3, _P, _STR3,
                                            _I32, _I32, _I32, _I32, _I32, _P, _F, _P, _I32,
                                            _P, ctypes.c_size_t, _P, _I64, _P],
+    "gqa_attention_decode_splitkv_noalloc": [_P, _STR3, _P, _STR3, _P, _STR3, _P, _STR3,
+                                             _I32, _I32, _I32, _I32, _I32, _P, _F, _P, _I32, _P],
     "gqa_attention_splitkv_partial": [_P, _STR3, _P, _STR3, _P, _STR3,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _P, _F, _I32, _I32,
                                       _P, ctypes.c_size_t, _P],

@@ -63,6 +63,14 @@ GQA_EXTERN_DISPATCH(256)
 
 }  // namespace gqa_host
 
+// Scratch of gqa_attention_decode_splitkv_noalloc: the split-KV partial
+// states live here instead of in a caller workspace.  Each GPU the library
+// runs on holds its own copy until the process ends.  Host code never passes
+// the name itself to a kernel (on the host it is a stand-in, not a device
+// address): the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using gqa_host::cdiv;
@@ -344,6 +352,50 @@ gqa_status_t gqa_attention_decode_splitkv_fused(
   a.tickets = tickets;
   GQA_TRY(run_partial(a, d, tile_s_kv, workspace, reinterpret_cast<hipStream_t>(stream)));
   return ok();
+}
+
+gqa_status_t gqa_attention_decode_splitkv_noalloc(
+    const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
+    const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3], int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t Skv, int32_t d, const int32_t* kv_len, float scale,
+    const float* sink, int32_t tile_s_kv, void* stream) {
+  // every host-side check first, so that no size or argument error touches
+  // a device
+  GQA_TRY(check_tile(tile_s_kv, true));
+  GQA_TRY(check_dense(q, q_stride, k, k_stride, v, v_stride, B, Hq, Hkv, 1, Skv, d, scale, 0));
+  const int64_t rows = (int64_t)B * Hq;
+  if (rows == 0) return ok();
+  GQA_TRY(check_ptr("o", o));
+  GQA_TRY(check_strides("o", o_stride, 3));
+  const size_t need = workspace_bytes_for(rows, Skv > 0 ? cdiv(Skv, tile_s_kv) : 1, d);
+  if (need > (size_t)GQA_NOALLOC_SCRATCH_BYTES)
+    return fail(GQA_ERR_WORKSPACE,
+                "no-alloc decode needs %zu bytes of partial states; the library's scratch holds "
+                "%zu (fewer rows or larger splits fit)",
+                need, (size_t)GQA_NOALLOC_SCRATCH_BYTES);
+  // the scratch's device address, looked up once per device with that
+  // device current; later calls reuse it
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(GQA_ERR_UNSUPPORTED, "device %d (up to 64 supported)", dev);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(GQA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      addr[dev] = p;
+    }
+    ws = addr[dev];
+  }
+  return gqa_attention_decode_splitkv(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq,
+                                      Hkv, Skv, d, kv_len, scale, sink, tile_s_kv, ws,
+                                      (size_t)GQA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 gqa_status_t gqa_attention_splitkv_partial(const void* q, const int64_t q_stride[3],

@@ -185,6 +185,31 @@ gqa_status_t gqa_attention_decode_splitkv_fused(
     int32_t* tickets, int64_t n_tickets, void* stream);
 
 /*
+ * gqa_attention_decode_splitkv for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, and the same
+ * kernels and result.  The split-KV partial states go into a scratch buffer
+ * of GQA_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU it runs on, kept until the process ends; the call itself
+ * allocates nothing.  A call whose partial states,
+ * gqa_attention_workspace_size(B, Hq, 1, Skv, d, tile_s_kv) bytes, exceed
+ * that size returns GQA_ERR_WORKSPACE before anything is enqueued (the
+ * decode of 16 sequences x 32 heads x 8192 keys in splits of 1024 needs
+ * 2,129,920 bytes).  Every call on one GPU shares its buffer, which keeps
+ * the last call's contents (nothing in it needs to start at zero): calls
+ * ordered on one stream are safe, calls that overlap in time on one GPU
+ * (other streams, other threads) race and give wrong results.  The first
+ * call on each device looks the buffer's address up (hipGetSymbolAddress)
+ * with that device current; make it once outside graph capture.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES (8u << 20)
+gqa_status_t gqa_attention_decode_splitkv_noalloc(
+    const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
+    const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3], int32_t B,
+    int32_t Hq, int32_t Hkv, int32_t Skv, int32_t d, const int32_t* kv_len, float scale,
+    const float* sink, int32_t tile_s_kv, void* stream);
+
+/*
  * The two phases of split-KV on their own, for callers that place the
  * partial states themselves (for instance KV sharded across devices, with
  * the partials gathered before one merge; the merge is associative -- see

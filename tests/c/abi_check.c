@@ -174,6 +174,25 @@ int main(void) {
                                               0.088f, NULL, 1024, P, 1024, T, 512, NULL),
            GQA_ERR_WORKSPACE);
   }
+  /* the allocation-free decode refuses partial states beyond its scratch
+   * (and every other bad argument) before touching a device */
+  expect("noalloc tile 0",
+         gqa_attention_decode_splitkv_noalloc(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,
+                                              0.088f, NULL, 0, NULL), GQA_ERR_INVALID_ARGUMENT);
+  expect("noalloc d 96",
+         gqa_attention_decode_splitkv_noalloc(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 96, NULL,
+                                              0.088f, NULL, 1024, NULL), GQA_ERR_UNSUPPORTED);
+  expect("noalloc NULL o",
+         gqa_attention_decode_splitkv_noalloc(P, s, P, s, P, s, NULL, s, 16, 32, 8, 8192, 128,
+                                              NULL, 0.088f, NULL, 1024, NULL),
+         GQA_ERR_INVALID_ARGUMENT);
+  /* 64 x 32 rows x 8 splits x 130 floats = 8,519,680 bytes > 8 MiB */
+  expect("noalloc beyond the scratch",
+         gqa_attention_decode_splitkv_noalloc(P, s, P, s, P, s, P, s, 64, 32, 8, 8192, 128, NULL,
+                                              0.088f, NULL, 1024, NULL), GQA_ERR_WORKSPACE);
+  expect("noalloc empty batch",
+         gqa_attention_decode_splitkv_noalloc(NULL, s, NULL, s, NULL, s, NULL, s, 0, 32, 8, 8192,
+                                              128, NULL, 0.088f, NULL, 1024, NULL), GQA_OK);
   printf("%s\n", failures ? "FAILED" : "ALL OK");
   return failures ? 1 : 0;
 }

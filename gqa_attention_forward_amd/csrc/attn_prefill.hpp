@@ -28,9 +28,14 @@
 // the row writes, the K operand reads and the transposing V reads are all
 // bank-conflict free (checked with the LDS bank-conflict counter).
 //
-// Each 64-key tile runs as four phases over its two 32-key halves, so the
-// softmax (vector ALU) of one half has the other half's MFMAs to hide
-// behind inside the wave:
+// The 8-wave form with one key group (d = 64, 128: causal and long prefill)
+// runs the two waves of each SIMD in ping-pong: each wave alternates an
+// MFMA-only phase (S of tile t, then P.V of tile t - 1) and a vector phase
+// (softmax of tile t, staging), the two waves of a SIMD half a tile apart,
+// with a workgroup barrier at every phase boundary (block "Ping-pong" below).
+// The other forms run each 64-key tile as four phases over its two 32-key
+// halves, so the softmax (vector ALU) of one half has the other half's MFMAs
+// to hide behind inside the wave:
 //   1. S_0 = K_0 Q^T
 //   2. S_1 = K_1 Q^T          || softmax of S_0
 //   3. O += V_0^T P_0^T       || softmax of S_1
@@ -381,6 +386,49 @@ attn_prefill_kernel(const AttnArgs a) {
     }
     return s;
   };
+  // S^T of both key halves with their MFMAs alternating, so each
+  // accumulator's consecutive MFMAs are apart (a wave's MFMA that reads the
+  // previous one's result waits for it); operands stream a few MFMAs ahead
+  // The MFMA-only phases keep their operand reads PD MFMAs ahead in program
+  // order (a scheduling barrier after each step): left free, the scheduler
+  // sinks each read next to its MFMA to save registers, and every MFMA then
+  // waits out a whole LDS latency.
+  auto qk2 = [&](const uint16_t* Ks, f32x16& s0, f32x16& s1) {
+    constexpr int PD = 3;
+    bf16x8 kb[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) kb[i] = kread(Ks, i >> 1, i & 1);
+    s0 = f32x16{};
+    s1 = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NCK; ++i) {
+      if (i & 1)
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[i % (PD + 1)], qf[i >> 1], s1, 0, 0, 0);
+      else
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[i % (PD + 1)], qf[i >> 1], s0, 0, 0, 0);
+      if (i + PD < 2 * NCK) kb[(i + PD) % (PD + 1)] = kread(Ks, (i + PD) >> 1, (i + PD) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // O^T += V^T P^T for both key halves, the same way (reads PD MFMAs ahead)
+  auto pv2 = [&](const uint16_t* Vs, const bf16x8 (&pb0)[2], const bf16x8 (&pb1)[2]) {
+    constexpr int NS = 4 * NDB;  // MFMA steps (half, t, db)
+    constexpr int PD = 3;
+    bf16x8 vb[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) vb[i] = vread(Vs, i / NDB, i % NDB);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const bf16x8& pb = (i / NDB) & 1 ? ((i / NDB) >> 1 ? pb1[1] : pb0[1])
+                                        : ((i / NDB) >> 1 ? pb1[0] : pb0[0]);
+      acc[i % NDB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % (PD + 1)], pb, acc[i % NDB], 0, 0, 0);
+      if (i + PD < NS) vb[(i + PD) % (PD + 1)] = vread(Vs, (i + PD) / NDB, (i + PD) % NDB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   // O^T += V^T P^T for keys 32 h .. 32 h + 31, next V operands in flight
   auto pv = [&](const uint16_t* Vs, int h, const bf16x8 (&pb)[2], auto interleave) {
     constexpr bool IL = decltype(interleave)::value;
@@ -437,6 +485,56 @@ attn_prefill_kernel(const AttnArgs a) {
       }
       pb[t] = __builtin_bit_cast(bf16x8, w);
     }
+    l = l * alpha + ls;
+    return alpha;
+  };
+  // Softmax of a whole 64-key tile (both halves against one reference):
+  // one max, one lazy reference decision, P rounded to bf16 and the row sum
+  // over the same rounded values.  Returns the O rescale factor.
+  auto softmax2 = [&](auto mask_tag, int j0, f32x16& s0, f32x16& s1, bf16x8 (&p0)[2],
+                      bf16x8 (&p1)[2]) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (MASK) {
+      // key offset o of the tile is masked iff o >= rem; the sign of
+      // rem - 1 - o gives an all-ones word for those, merged bitwise (no
+      // compare results to hold in scalar registers across the tile)
+      const int rem1 = lim - j0 - 8 * hl - 1;
+      constexpr uint32_t kNegInf = 0xff800000u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t m0 = (uint32_t)((rem1 - (16 * (j >> 3) + (j & 7))) >> 31);
+        const uint32_t m1 = (uint32_t)((rem1 - (32 + 16 * (j >> 3) + (j & 7))) >> 31);
+        s0[j] = __uint_as_float((m0 & kNegInf) | (~m0 & __float_as_uint(s0[j])));
+        s1[j] = __uint_as_float((m1 & kNegInf) | (~m1 & __float_as_uint(s1[j])));
+      }
+    }
+    float m = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int j = 1; j < 16; ++j) m = vmax(vmax(m, s0[j]), s1[j]);
+    const float mx = half_swap_max(m) * a.scale_log2;
+    mtrue = fmaxf(mtrue, mx);
+    const bool move = mx > mref + kLazyRescale;
+    const float alpha = move ? ex2(mref - mx) : 1.f;  // 0 when mref = -inf
+    mref = move ? mx : mref;
+    const float mu = (mref == -INFINITY) ? 0.f : mref;
+    float ls = 0.f;
+    auto expo = [&](const f32x16& sv, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 x = {ex2(__builtin_fmaf(sv[8 * t + 2 * e], a.scale_log2, -mu)),
+                           ex2(__builtin_fmaf(sv[8 * t + 2 * e + 1], a.scale_log2, -mu))};
+          const bf16x2 pp = __builtin_convertvector(x, bf16x2);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
+          w[e] = __builtin_bit_cast(uint32_t, pp);
+        }
+        pb[t] = __builtin_bit_cast(bf16x8, w);
+      }
+    };
+    expo(s0, p0);
+    expo(s1, p1);
     l = l * alpha + ls;
     return alpha;
   };
@@ -576,8 +674,126 @@ attn_prefill_kernel(const AttnArgs a) {
     lds_barrier();
   };
 
+  // ---- Ping-pong of the two waves of each SIMD (8 waves, one key group,
+  // d <= 128).  A wave issues in order, and an MFMA holds its wave until the
+  // matrix pipe takes it, so vector work placed between a wave's own MFMAs
+  // mostly adds to its time; vector work of ANOTHER wave on the same SIMD
+  // runs under those MFMAs for free (measured on gfx950 with register-only
+  // loops: MFMA and FMA mixed in both waves of a SIMD took the sum of their
+  // times, one wave of each took the MFMA time alone).  So each wave
+  // alternates two pure phases:
+  //   M(t): S = K_t Q^T (both halves), then O += V_{t-1}^T P_{t-1}^T  (MFMA
+  //         and LDS operand reads only)
+  //   V(t): softmax of S_t -> P_t and the O rescale, then this thread's
+  //         share of the next tiles' staging (LDS writes, global loads)
+  // and waves 4-7 run one phase behind waves 0-3; wave w and wave w + 4 share
+  // a SIMD, so one is always in M while the other is in V.  A barrier ends
+  // every phase ("slot"); both halves pass 2 ntl + 1 of them (the lagging
+  // half starts with a slot of staging only, the leading half ends with a
+  // barrier after its last M).
+  //
+  // Tile t's K is read in slots 2t (leading half) and 2t + 1 (lagging), its
+  // V in slots 2t + 2 and 2t + 3.  The V phase of tile u stores K(u+1) and
+  // V(u) (leading, slot 2u + 1) or K(u+2) and V(u+1) (lagging, slot 2u + 2)
+  // into the stages of those tiles, each after the previous occupant's last
+  // reader and before the first reader; it then requests the shares its next
+  // V phase stores, two slots ahead.  Past the last tile the loads go through
+  // empty resources (zeros) and land in stage areas no wave reads again.
+  constexpr bool PP = EARLY && NW == 8 && KS == 1;
+  if constexpr (PP) {
+    const int lagh = (wv >> 2) & 1;  // wave-uniform: 1 = the lagging half
+    u32x4 rk[CPT], rv[CPT];          // staged shares: one K tile, one V tile
+    auto share_res = [&](int T, bool isk) __attribute__((always_inline)) {
+      const int j0 = tile_key(max(0, min(T, ntl - 1)));  // in the page table even past the end
+      int64_t off;
+      if constexpr (PAGED)
+        off = (int64_t)ptab[(int64_t)b * a.max_pages + (j0 >> 6)] * a.kv_sp;
+      else
+        off = (int64_t)j0 * (isk ? a.k_ss : a.v_ss);
+      const uint32_t rs2 = isk ? kss2 : vss2;
+      const uint32_t valid = (uint32_t)min(BK, n - j0);
+      return make_bufres((isk ? khead : vhead) + off,
+                         T < ntl ? (valid - 1u) * rs2 + (uint32_t)D * 2u : 0u);
+    };
+    auto stage_load = [&](int tk, int tv) __attribute__((always_inline)) {
+      const BufRes kr = share_res(tk, true);
+      const BufRes vr = share_res(tv, false);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        rk[i] = buf_load16v<CP>(kr, koff[i]);
+        rv[i] = buf_load16v<CP>(vr, voff[i]);
+      }
+    };
+    auto stage_store = [&](int tk, int tv) __attribute__((always_inline)) {
+      uint16_t* Kd = sg + (tk & 1) * C::STAGE + kst;
+      uint16_t* Vd = sg + (tv & 1) * C::STAGE + C::KTILE + vst;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        *reinterpret_cast<u32x4*>(Kd + i * (NTH / DC) * C::KP) = rk[i];
+        *reinterpret_cast<u32x4*>(Vd + i * (NTH / DC) * D) = rv[i];
+      }
+    };
+    f32x16 ps0, ps1;     // S of the tile between its M and V phases
+    bf16x8 pp0[2], pp1[2];  // P of the tile between its V phase and the next M
+    auto m_qk = [&](auto par) __attribute__((always_inline)) {
+      qk2(sg + decltype(par)::value * C::STAGE, ps0, ps1);
+    };
+    auto m_pv = [&](auto par) __attribute__((always_inline)) {
+      pv2(sg + decltype(par)::value * C::STAGE + C::KTILE, pp0, pp1);
+    };
+    auto v_phase = [&](auto mask_tag, int u) __attribute__((always_inline)) {
+      rescale(softmax2(mask_tag, tile_key(u), ps0, ps1, pp0, pp1));
+      stage_store(u + 1 + lagh, u + lagh);
+      stage_load(u + 2 + lagh, u + 1 + lagh);
+    };
+    // tile u's V phase, then M(u + 1): the next tile's QK^T and tile u's
+    // P.V.  After the last tile the QK^T runs on whatever the idle stage
+    // holds and its S is never used (one branch-free step: two copies of the
+    // phase cost more registers than the 16 MFMAs once per workgroup).
+    auto pp_step = [&](auto mask_tag, int u, auto par) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par)::value;
+      v_phase(mask_tag, u);
+      lds_barrier();
+      m_qk(std::integral_constant<int, 1 - PAR>{});
+      m_pv(std::integral_constant<int, PAR>{});
+      if (!(lagh && u == ntl - 1)) lds_barrier();  // the lagging half has one fewer here
+    };
+    if (ntl > 0) {
+      stage_load(1, 0);
+      if (lagh) {  // slot 0: the lagging half's staging only
+        stage_store(1, 0);
+        stage_load(2, 1);
+        lds_barrier();
+      }
+      m_qk(std::integral_constant<int, 0>{});  // M(0): no P.V yet
+      lds_barrier();
+      using P0 = std::integral_constant<int, 0>;
+      using P1 = std::integral_constant<int, 1>;
+      int u = 0;
+      for (; u + 1 < nfull; u += 2) {
+        pp_step(False{}, u, P0{});
+        pp_step(False{}, u + 1, P1{});
+      }
+      if (u < nfull) {  // odd number of unmasked tiles
+        pp_step(False{}, u, P0{});
+        ++u;
+        if (u < ntl) {
+          pp_step(True{}, u, P1{});
+          ++u;
+        }
+      }
+      for (; u + 1 < ntl; u += 2) {
+        pp_step(True{}, u, P0{});
+        pp_step(True{}, u + 1, P1{});
+      }
+      if (u < ntl) pp_step(True{}, u, P0{});
+    }
+  }
+
   int it = 0;
-  if constexpr (EARLY) {
+  if constexpr (PP) {
+    // done above
+  } else if constexpr (EARLY) {
     // Tiles two at a time (stages 0 and 1), unmasked tiles first, then the
     // masked ones; a leftover single tile runs on its own stage.  (The
     // forms without the early fetch keep a runtime stage: unrolled, they

@@ -254,10 +254,13 @@ def bench_decode(args, device, stream):
     # the merge kernel runs a few microseconds: time it from a captured graph
     ms_m = time_graph(merge, 20, 5, stream)
     assert torch.isfinite(out.float()).all()
+    rf = roof("hbm", read_bytes / (ms_p * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", measured_traffic())
+    # the dominant kernel's fraction is `frac`; the whole step's (partial +
+    # merge kernels, the headline value) is reported beside it
+    rf["step_frac"] = round(gbs / HBM_PEAK_GBS, 4)
     return c, inp, {
         "ms_per_step": ms, "value": gbs, "total_bytes": total_bytes,
-        "roofline": roof("hbm", read_bytes / (ms_p * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                         measured_traffic()),
+        "roofline": rf,
         "kernel_ms": {"partial": round(ms_p, 5), "merge": round(ms_m, 5)},
         "kernel_bytes_per_launch": {"partial": read_bytes},
     }
@@ -510,33 +513,120 @@ def run_only(args, device, stream):
             "GB/s": dense_bytes(c)[0] / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline(inp, c, budget_s):
-    """The oracle on this host's cores, cycling over whole decode sequences
-    (all heads and keys of one sequence per call) until ~budget_s seconds of
-    oracle time; fp64 input conversion is outside the timed region."""
-    import oracle
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(inp, c, budget_s):
+    """The oracle on this host's cores (never tuned for this), input conversion
+    outside the timed regions.  The headline figure cycles over whole decode
+    sequences (all heads and keys of one sequence per call) for about half the
+    budget; the other configs get the rest:
+      tiny prefill and ragged paged: one full evaluation each;
+      short-q/long-kv: whole (b, kv head) groups (all G heads x 16 rows x 16384
+        keys), cycling, for about a sixth of the budget;
+      causal prefill: rows spread over the sequence (each over its visible
+        keys), cycling, for about a sixth of the budget.
+    Each entry reports the throughput in the workload's own unit and the
+    sample it was measured on."""
+    import oracle
+    threads = _oracle_threads()
+    per = {}
+    # decode (headline): whole sequences
     elapsed, done = 0.0, 0
     cache = {}
-    while elapsed < budget_s:
+    while elapsed < budget_s / 2:
         b = done % c.B
         if b not in cache:
             cache[b] = tuple(t[b:b + 1].to(torch.float64).numpy()
                              for t in (inp["q"], inp["k"], inp["v"]))
         qb, kb, vb = cache[b]
-        t0 = time.perf_counter()
-        oracle.attention_fp64(qb, kb, vb, scale=inp["scale"])
-        elapsed += time.perf_counter() - t0
+        elapsed += _timed(lambda: oracle.attention_fp64(qb, kb, vb, scale=inp["scale"]))
         done += 1
     per_seq = (2 * c.Hq * c.d * 2) + 2 * c.Hkv * c.Skv * c.d * 2
-    return {"value": round(done * per_seq / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} decode sequences of the decode_splitkv workload (cycling over its "
-                      f"{c.B}; each all {c.Hq} heads x {c.Skv} keys), {elapsed:.1f} s of oracle time"}
+    dec_gbs = done * per_seq / elapsed / 1e9
+    per["decode_splitkv"] = {"value": round(dec_gbs, 4), "unit": "GB/s",
+                             "sample": f"{done} whole sequences (of {c.B}), {elapsed:.1f} s"}
+    # tiny prefill: in full
+    ct = workloads.CASES["tiny_prefill"]
+    t = workloads.make_case(ct)
+    f64 = [x.to(torch.float64).numpy() for x in (t["q"], t["k"], t["v"])]
+    sec = min(_timed(lambda: oracle.attention_fp64(*f64, scale=t["scale"])) for _ in range(5))
+    per["tiny_prefill"] = {"value": round(sec * 1e3, 4), "unit": "ms per call",
+                           "sample": "the whole workload (best of 5 calls)"}
+    # short-q / long-kv: whole (b, kv head) groups
+    cs = workloads.CASES["shortq_longkv"]
+    t = workloads.make_case(cs)
+    q64, k64, v64 = (x.to(torch.float64).numpy() for x in (t["q"], t["k"], t["v"]))
+    G = cs.Hq // cs.Hkv
+    elapsed, done = 0.0, 0
+    while elapsed < budget_s / 6:
+        b, g = (done // cs.Hkv) % cs.B, done % cs.Hkv
+        qs = q64[b:b + 1, g * G:(g + 1) * G]
+        ks, vs = k64[b:b + 1, g:g + 1], v64[b:b + 1, g:g + 1]
+        elapsed += _timed(lambda: oracle.attention_fp64(qs, ks, vs, scale=t["scale"]))
+        done += 1
+    grp_flops = 4 * cs.d * G * cs.Sq * cs.Skv
+    grp_bytes = (2 * G * cs.Sq + 2 * cs.Skv) * cs.d * 2
+    per["shortq_longkv"] = {"value": round(done * grp_bytes / elapsed / 1e9, 4), "unit": "GB/s",
+                            "TFLOP/s": round(done * grp_flops / elapsed / 1e12, 6),
+                            "sample": f"{done} (b, kv head) groups of {cs.B * cs.Hkv}, "
+                                      f"{elapsed:.1f} s"}
+    del q64, k64, v64, t
+    # causal prefill: rows spread over the sequence
+    cc = workloads.CASES["causal_prefill"]
+    t = workloads.make_case(cc)
+    q64, k64, v64 = (x.to(torch.float64).numpy() for x in (t["q"], t["k"], t["v"]))
+    rng = np.random.default_rng(0)
+    elapsed, rows, flops = 0.0, 0, 0
+    while elapsed < budget_s / 6:
+        n = 64
+        bi = rng.integers(0, cc.B, n)
+        hi = rng.integers(0, cc.Hq, n)
+        ii = rng.integers(0, cc.Sq, n)
+        elapsed += _timed(lambda: oracle.attention_rows_fp64(q64, k64, v64, bi, hi, ii,
+                                                             scale=t["scale"], causal=True))
+        rows += n
+        flops += int((4 * cc.d * (ii + 1)).sum())
+    per["causal_prefill"] = {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s",
+                             "sample": f"{rows} rows drawn over the sequence (of "
+                                       f"{cc.B * cc.Hq * cc.Sq}), {elapsed:.1f} s"}
+    del q64, k64, v64, t
+    # ragged paged: in full
+    w = workloads.make_paged()
+    args = [workloads.to_f64(w["q"]), w["cu_seqlens_q"].numpy(), workloads.to_f64(w["k_cache"]),
+            workloads.to_f64(w["v_cache"]), w["page_table"].numpy(), w["kv_len"].numpy()]
+    sec = _timed(lambda: oracle.paged_attention_fp64(*args, scale=w["scale"], page_size=64,
+                                                      sink=workloads.to_f64(w["sink"])))
+    pb, pf = paged_work(w)
+    per["ragged_paged"] = {"value": round(sec * 1e3, 3), "unit": "ms per call",
+                           "TFLOP/s": round(pf / sec / 1e12, 6),
+                           "sample": "the whole workload (one call)"}
+    return {"value": round(dec_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": per["decode_splitkv"]["sample"] + " of the decode_splitkv workload (each "
+                      f"all {c.Hq} heads x {c.Skv} keys)",
+            "per_config": per}
 
 
 def main():
@@ -547,7 +637,7 @@ def main():
     # read 85 us, after 200 or 1000 it reads 81.3-81.7 us
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=18.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--only", choices=["decode_partial", "shortq_longkv", "causal_prefill",
                                        "ragged_paged", "ragged_paged_onepass",

@@ -356,16 +356,19 @@ def bench_secondary(args, device, stream):
         "roofline": roof("hbm", tb / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
     del g, outf, wsf, tk
     fresh_allocations()
-    # the other head dims: decode at d = 256, causal prefill at d = 32 and 256
-    c, _, g = setup_dense("decode_splitkv_d256", device)
-    step, _, _, _ = decode_step_fns(g, c)
-    ms = time_loop(step, steps, warm_steps(step, stream), stream)
-    tb, _ = dense_bytes(c)
-    res["decode_splitkv_d256"] = {
-        "ms": round(ms, 5), "GB/s": round(tb / (ms * 1e-3) / 1e9, 1),
-        "roofline": roof("hbm", tb / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
-    del g
-    for name in ("causal_prefill_d32", "causal_prefill_d256"):
+    # the other head dims: decode at d = 256 and 512, causal prefill at d = 32,
+    # 256 and 512
+    for name in ("decode_splitkv_d256", "decode_splitkv_d512"):
+        c, _, g = setup_dense(name, device)
+        step, _, _, _ = decode_step_fns(g, c)
+        ms = time_loop(step, steps, warm_steps(step, stream), stream)
+        tb, _ = dense_bytes(c)
+        res[name] = {
+            "ms": round(ms, 5), "GB/s": round(tb / (ms * 1e-3) / 1e9, 1),
+            "roofline": roof("hbm", tb / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+        del g
+        fresh_allocations()
+    for name in ("causal_prefill_d32", "causal_prefill_d256", "causal_prefill_d512"):
         c, _, g = setup_dense(name, device)
         step, out = prefill_step_fn(g, c, 0)
         ms = time_loop(step, steps, warm_steps(step, stream), stream)
@@ -507,7 +510,10 @@ def run_only(args, device, stream):
         return {"workload": name, "ms": ms,
                 "TFLOP/s": paged_work(w, causal=True)[1] / (ms * 1e-3) / 1e12}
     c, _, g = setup_dense(name, device)
-    step, _ = prefill_step_fn(g, c, 2048 if name == "shortq_longkv" else 0)
+    if c.decode:
+        step, _, _, _ = decode_step_fns(g, c)
+    else:
+        step, _ = prefill_step_fn(g, c, 2048 if name == "shortq_longkv" else 0)
     ms = time_loop(step, args.steps, args.warmup, stream)
     return {"workload": name, "ms": ms, "TFLOP/s": dense_flops(c) / (ms * 1e-3) / 1e12,
             "GB/s": dense_bytes(c)[0] / (ms * 1e-3) / 1e9}
@@ -642,7 +648,8 @@ def main():
     ap.add_argument("--only", choices=["decode_partial", "shortq_longkv", "causal_prefill",
                                        "ragged_paged", "ragged_paged_onepass",
                                        "paged_causal_chunked", "paged_decode",
-                                       "paged_decode_append", "copy"],
+                                       "paged_decode_append", "copy",
+                                       *workloads.HEAD_DIM_CASES],
                     help="profiling aid: time only this workload's kernels and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -19,8 +19,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", name) for name in
-           ("dispatch_d128.hip", "dispatch_d256.hip", "dispatch_d64.hip", "dispatch_d32.hip",
-            "gqa_api.hip")]
+           ("dispatch_d128.hip", "dispatch_d256.hip", "dispatch_d512.hip", "dispatch_d64.hip",
+            "dispatch_d32.hip", "gqa_api.hip")]
 OUT = os.path.join(HERE, "libgqa.so")
 
 HIPCC_FLAGS = [

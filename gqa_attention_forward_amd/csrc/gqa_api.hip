@@ -60,6 +60,10 @@ GQA_EXTERN_DISPATCH(32)
 GQA_EXTERN_DISPATCH(64)
 GQA_EXTERN_DISPATCH(128)
 GQA_EXTERN_DISPATCH(256)
+extern template gqa_status_t dispatch_wide<false, false>(gqa::AttnArgs, int64_t, hipStream_t);
+extern template gqa_status_t dispatch_wide<false, true>(gqa::AttnArgs, int64_t, hipStream_t);
+extern template gqa_status_t dispatch_wide<true, false>(gqa::AttnArgs, int64_t, hipStream_t);
+extern template gqa_status_t dispatch_wide<true, true>(gqa::AttnArgs, int64_t, hipStream_t);
 
 }  // namespace gqa_host
 
@@ -76,6 +80,7 @@ namespace {
 using gqa_host::cdiv;
 using gqa_host::check_launch;
 using gqa_host::dispatch_rows;
+using gqa_host::dispatch_wide;
 using gqa_host::fail;
 
 gqa_status_t ok() {
@@ -109,13 +114,13 @@ gqa_status_t check_scale(float scale) {
   return GQA_OK;
 }
 
-bool head_dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+bool head_dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 256 || d == 512; }
 
 gqa_status_t check_heads(int32_t Hq, int32_t Hkv, int32_t d) {
   if (Hq < 1 || Hkv < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "Hq and Hkv must be >= 1");
   if (Hq % Hkv != 0)
     return fail(GQA_ERR_INVALID_ARGUMENT, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
-  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 32, 64, 128, 256)", d);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 32, 64, 128, 256, 512)", d);
   return GQA_OK;
 }
 
@@ -138,7 +143,8 @@ gqa_status_t dispatch(gqa::AttnArgs args, int d, int64_t rows, hipStream_t strea
     case 32: return dispatch_rows<32, PAGED, PARTIAL>(args, rows, stream);
     case 64: return dispatch_rows<64, PAGED, PARTIAL>(args, rows, stream);
     case 128: return dispatch_rows<128, PAGED, PARTIAL>(args, rows, stream);
-    default: return dispatch_rows<256, PAGED, PARTIAL>(args, rows, stream);
+    case 256: return dispatch_rows<256, PAGED, PARTIAL>(args, rows, stream);
+    default: return dispatch_wide<PAGED, PARTIAL>(args, rows, stream);
   }
 }
 
@@ -157,11 +163,13 @@ gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int
   auto kern = sparse ? (d == 32 ? gqa::merge_kernel<32, true>
                         : d == 64 ? gqa::merge_kernel<64, true>
                         : d == 128 ? gqa::merge_kernel<128, true>
-                                   : gqa::merge_kernel<256, true>)
+                        : d == 256 ? gqa::merge_kernel<256, true>
+                                   : gqa::merge_kernel<512, true>)
                      : (d == 32 ? gqa::merge_kernel<32, false>
                         : d == 64 ? gqa::merge_kernel<64, false>
                         : d == 128 ? gqa::merge_kernel<128, false>
-                                   : gqa::merge_kernel<256, false>);
+                        : d == 256 ? gqa::merge_kernel<256, false>
+                                   : gqa::merge_kernel<512, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(256), 0, stream, ml, ot,
                      reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq, n_split,
                      rows);
@@ -334,6 +342,7 @@ gqa_status_t gqa_attention_decode_splitkv_fused(
   if (Hq / Hkv > 32)
     return fail(GQA_ERR_UNSUPPORTED, "in-kernel merge handles groups of up to 32 heads (G = %d)",
                 Hq / Hkv);
+  if (d == 512) return fail(GQA_ERR_UNSUPPORTED, "in-kernel merge handles head dims up to 256");
   const int64_t rows = (int64_t)B * Hq;
   if (rows == 0) return ok();
   GQA_TRY(check_ptr("o", o));
@@ -423,7 +432,7 @@ gqa_status_t gqa_attention_splitkv_merge(const void* workspace, size_t workspace
                                          const float* sink, void* stream) {
   if (B < 0 || Sq < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "B and Sq must be >= 0");
   if (Hq < 1 || n_split < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "Hq and n_split must be >= 1");
-  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 32, 64, 128, 256)", d);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d (supported: 32, 64, 128, 256, 512)", d);
   const int64_t rows = (int64_t)B * Hq * Sq;
   if (rows == 0) return ok();
   GQA_TRY(check_ptr("o", o));
@@ -456,6 +465,7 @@ gqa_status_t paged_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   GQA_TRY(check_scale(scale));
   if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   GQA_TRY(check_tile(tile_s_kv, false));
+  if (append && d == 512) return fail(GQA_ERR_UNSUPPORTED, "append handles head dims up to 256");
   if (append && (int64_t)max_q_len * (Hq / Hkv) > 32)
     return fail(GQA_ERR_UNSUPPORTED,
                 "append handles up to 32 query rows per kv head (max_q_len %d x group %d)",

@@ -25,6 +25,10 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 template <int D, bool PAGED, bool PARTIAL>
 gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream);
 
+// The same at head dim 512 (dispatch_d512.hip): one form for every row count.
+template <bool PAGED, bool PARTIAL>
+gqa_status_t dispatch_wide(gqa::AttnArgs args, int64_t rows, hipStream_t stream);
+
 #define GQA_EXTERN_DISPATCH(D)                                                              \
   extern template gqa_status_t dispatch_rows<D, false, false>(gqa::AttnArgs, int64_t,       \
                                                               hipStream_t);                 \

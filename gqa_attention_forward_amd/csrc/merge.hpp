@@ -79,7 +79,11 @@ merge_kernel(const float2* __restrict__ ml, const float* __restrict__ ot, uint16
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = (M == -INFINITY) ? 0.f : accv[e] * inv;
   uint16_t* op = o + b * o_sb + (int64_t)h * o_sh + (int64_t)i * o_ss + lane * E;
-  if constexpr (E == 4) {
+  if constexpr (E == 8) {
+    *reinterpret_cast<uint4*>(op) =
+        make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
+                   pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+  } else if constexpr (E == 4) {
     *reinterpret_cast<uint2*>(op) =
         make_uint2(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]));
   } else if constexpr (E == 2) {

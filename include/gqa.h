@@ -52,9 +52,11 @@
  *    kv_stride_row, the append form's new_stride_t) must be below 2^25
  *    elements, else GQA_ERR_UNSUPPORTED: a 64-key tile is addressed with
  *    32-bit byte offsets from its first row.
- *    d must be 32, 64, 128 or 256, else GQA_ERR_UNSUPPORTED (the AstrAI
- *    commit log's kernels cover prefill at head dim 32 and decode at 256
- *    besides 64 and 128).  A launch whose grid would exceed 2^32 - 1
+ *    d must be 32, 64, 128, 256 or 512, else GQA_ERR_UNSUPPORTED (the
+ *    AstrAI commit log's kernels cover prefill at head dim 32 and decode at
+ *    256 besides 64 and 128; the nvfp4-megamoe-kernel commit log's sweep
+ *    reaches 512).  The in-kernel merge and the append form take d up to
+ *    256.  A launch whose grid would exceed 2^32 - 1
  *    work-items (one dispatch's limit) also returns GQA_ERR_UNSUPPORTED.
  *
  * Ownership: the caller owns all memory and keeps it alive until the work
@@ -89,7 +91,7 @@ typedef int32_t gqa_status_t;
 
 #define GQA_OK 0
 #define GQA_ERR_INVALID_ARGUMENT 1 /* NULL required pointer, bad dims, Hq % Hkv != 0, bad flag */
-#define GQA_ERR_UNSUPPORTED 2      /* d not 32/64/128/256, misaligned pointer or stride,
+#define GQA_ERR_UNSUPPORTED 2      /* d not 32/64/128/256/512, misaligned pointer or stride,
                                       page_size != 64, a group beyond the append/fused limits,
                                       a grid beyond 2^32 - 1 work-items */
 #define GQA_ERR_WORKSPACE 3        /* workspace NULL or too small; ticket array too small */

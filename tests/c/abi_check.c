@@ -79,6 +79,7 @@ int main(void) {
                                0, NULL), GQA_ERR_WORKSPACE);
   }
   expect("d = 96", PREFILL(P, s, 96, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
+  expect("d = 1024", PREFILL(P, s, 1024, 4, 1, 0.125f, 0, 0, NULL, 0), GQA_ERR_UNSUPPORTED);
   expect("Hq % Hkv", PREFILL(P, s, 64, 6, 4, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("Hkv = 0", PREFILL(P, s, 64, 4, 0, 0.125f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("scale 0", PREFILL(P, s, 64, 4, 1, 0.0f, 0, 0, NULL, 0), GQA_ERR_INVALID_ARGUMENT);
@@ -118,7 +119,7 @@ int main(void) {
   expect("paged NULL cu", PAGED(NULL, P, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("paged NULL table", PAGED(P, NULL, P, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
   expect("paged NULL kv_len", PAGED(P, P, NULL, 64, 128, 0), GQA_ERR_INVALID_ARGUMENT);
-  expect("paged d 512", PAGED(P, P, P, 64, 512, 0), GQA_ERR_UNSUPPORTED);
+  expect("paged d 1024", PAGED(P, P, P, 64, 1024, 0), GQA_ERR_UNSUPPORTED);
   expect("paged d 48", PAGED(P, P, P, 64, 48, 0), GQA_ERR_UNSUPPORTED);
   expect("paged causal 3", PAGED(P, P, P, 64, 128, 3), GQA_ERR_INVALID_ARGUMENT);
   expect("paged split, no workspace",
@@ -139,6 +140,11 @@ int main(void) {
   expect("append misaligned k_new", APPEND(M, P, 1024, 1), GQA_ERR_UNSUPPORTED);
   expect("append new stride 1020", APPEND(P, P, 1020, 1), GQA_ERR_UNSUPPORTED);
   expect("append 36 rows per kv head", APPEND(P, P, 1024, 9), GQA_ERR_UNSUPPORTED);
+  expect("append d 512",
+         gqa_attention_paged_append(P, 4096, 128, P, P, P, 8192, 128, 128, P, 64, P, P, P, 1024,
+                                    128, P, 4096, 128, 8, 32, 8, 512, 64, 8, 1, 0.044f, NULL, 0, 0,
+                                    NULL, 0, NULL),
+         GQA_ERR_UNSUPPORTED);
   expect("append new stride 2^26", APPEND(P, P, (int64_t)1 << 26, 1), GQA_ERR_UNSUPPORTED);
   expect("append new stride 2^25", APPEND(P, P, (int64_t)1 << 25, 1), GQA_ERR_UNSUPPORTED);
   expect("append new stride 2^25 - 8 passes (stops at the workspace)",
@@ -164,6 +170,10 @@ int main(void) {
     expect("fused group 64",
            gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 64, 1, 8192, 128, NULL,
                                               0.088f, NULL, 1024, P, 1 << 30, T, 1024, NULL),
+           GQA_ERR_UNSUPPORTED);
+    expect("fused d 512",
+           gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 512, NULL,
+                                              0.044f, NULL, 1024, P, 1 << 30, T, 512, NULL),
            GQA_ERR_UNSUPPORTED);
     expect("fused tile 0",
            gqa_attention_decode_splitkv_fused(P, s, P, s, P, s, P, s, 16, 32, 8, 8192, 128, NULL,

@@ -99,6 +99,7 @@ def _rows(c, n, seed):
 # the benchmark times (decode: splits of 1024; short-q: splits of 2048, and
 # one pass), compared with the oracle at every output element.
 @pytest.mark.parametrize("name,tile", [("decode_splitkv", 1024), ("decode_splitkv_d256", 1024),
+                                       ("decode_splitkv_d512", 1024),
                                        ("shortq_longkv", 2048), ("shortq_longkv", 0)])
 def test_full_size_in_full(name, tile):
     c = workloads.CASES.get(name) or workloads.HEAD_DIM_CASES[name]
@@ -130,7 +131,8 @@ def causal_block_rows(c, seed):
     return np.array(bb), np.array(hh), np.array(ii)
 
 
-@pytest.mark.parametrize("name", ["causal_prefill", "causal_prefill_d32", "causal_prefill_d256"])
+@pytest.mark.parametrize("name", ["causal_prefill", "causal_prefill_d32", "causal_prefill_d256",
+                                  "causal_prefill_d512"])
 def test_causal_full_size_every_workgroup(name):
     c = workloads.CASES.get(name) or workloads.HEAD_DIM_CASES[name]
     note(f"{name} full size {c}")
@@ -381,10 +383,12 @@ def test_sweep(shape, causal, tile):
     assert_close(got, want, f"{shape} c={causal} t={tile}")
 
 
-# head dims 32 and 256 (AstrAI commit log: scalar prefill at d = 32, scalar
-# decode at d = 256), through every kernel form: one 16-column block (rows
-# <= 16), two (rows <= 32; two q-tiles at d = 256), and the shared-tile
-# prefill kernel at 2 and 4 waves (d = 32) or 4 waves (d = 256)
+# head dims 32, 256 and 512 (AstrAI commit log: scalar prefill at d = 32,
+# scalar decode at d = 256; nvfp4-megamoe-kernel commit log: head dims up to
+# 512), through every kernel form: one 16-column block (rows <= 16), two
+# (rows <= 32; two q-tiles at d = 256), the shared-tile prefill kernel at 2
+# and 4 waves (d = 32) or 4 waves (d = 256), and the split-head-dim kernel
+# (d = 512, 32 rows per workgroup)
 SWEEP_HD = [
     # B, Hq, Hkv, Sq, Skv
     (2, 8, 2, 1, 500),
@@ -395,7 +399,7 @@ SWEEP_HD = [
 ]
 
 
-@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("d", [32, 256, 512])
 @pytest.mark.parametrize("shape", SWEEP_HD)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tile", [0, 64, 192])
@@ -409,7 +413,7 @@ def test_sweep_head_dims(d, shape, causal, tile):
     assert_close(got, want, f"d={d} {shape} c={causal} t={tile}")
 
 
-@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("d", [32, 256, 512])
 @pytest.mark.parametrize("tile", [1024, 64])
 def test_decode_head_dims(d, tile):
     note(f"decode d={d} tile={tile}")
@@ -467,7 +471,7 @@ def test_decode_fused_full_size():
     assert_close(out, oracle_dense(inp, use_sink=False), "fused decode full size, every element")
 
 
-@pytest.mark.parametrize("d", [32, 256])
+@pytest.mark.parametrize("d", [32, 256, 512])
 @pytest.mark.parametrize("causal", [False, True])
 def test_paged_head_dims(d, causal):
     note(f"paged d={d} causal={causal}")

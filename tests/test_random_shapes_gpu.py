@@ -36,7 +36,7 @@ def to_dev(inp):
 
 
 def _dense_case(r, seed):
-    d = r.choice([32, 64, 128, 256])
+    d = r.choice([32, 64, 128, 256, 512])
     G = r.choice([1, 2, 3, 4, 5, 8, 16, 32])
     Hkv = r.choice([1, 2, 3])
     B = r.randint(1, 3)
@@ -45,7 +45,7 @@ def _dense_case(r, seed):
     tile = r.choice([0, 0, 64, 128, 320, 1024])
     use_sink = r.random() < 0.5
     decode = Sq == 1 and tile > 0 and r.random() < 0.5
-    fused = decode and G <= 32 and r.random() < 0.5
+    fused = decode and G <= 32 and d <= 256 and r.random() < 0.5
     causal = (not decode) and r.random() < 0.5
     what = (f"dense d={d} G={G} Hkv={Hkv} B={B} Sq={Sq} Skv={Skv} causal={causal} tile={tile} "
             f"sink={use_sink} decode={decode} fused={fused} seed={seed}")
@@ -71,13 +71,13 @@ def _dense_case(r, seed):
 
 
 def _paged_case(r, seed):
-    d = r.choice([32, 64, 128, 256])
+    d = r.choice([32, 64, 128, 256, 512])
     G = r.choice([1, 2, 3, 4, 5, 8, 16, 32])
     Hkv = r.choice([1, 2, 3])
     B = r.randint(1, 4)
     causal = r.random() < 0.5
     tile = r.choice([0, 0, 64, 128, 320, 1024])
-    append = r.random() < 0.4
+    append = d <= 256 and r.random() < 0.4
     top = max(1, 32 // G) if append else r.choice([1, 4, 40])
     q_lens = [r.randint(0 if r.random() < 0.1 else 1, top) for _ in range(B)]
     if sum(q_lens) == 0:

@@ -73,8 +73,8 @@ PAGED_SEED = 1005
 CHUNKED_SEED = 1006
 
 # The same decode and causal prefill shapes at the other head dims the pages'
-# kernels cover (decode at d = 256, prefill at d = 32); measured beside the
-# named workloads.
+# kernels cover (decode at d = 256, prefill at d = 32, and d = 512); measured
+# beside the named workloads.
 HEAD_DIM_CASES = {
     "decode_splitkv_d256": DenseCase("decode_splitkv_d256", 16, 32, 8, 1, 8192, 256,
                                      tile_s_kv=1024, decode=True, seed=1008),
@@ -82,6 +82,11 @@ HEAD_DIM_CASES = {
                                     causal=True, seed=1009),
     "causal_prefill_d256": DenseCase("causal_prefill_d256", 2, 32, 8, 8192, 8192, 256,
                                      causal=True, seed=1010),
+    # d = 512 (the nvfp4-megamoe-kernel sweep's widest head)
+    "decode_splitkv_d512": DenseCase("decode_splitkv_d512", 16, 32, 8, 1, 8192, 512,
+                                     tile_s_kv=1024, decode=True, seed=1012),
+    "causal_prefill_d512": DenseCase("causal_prefill_d512", 2, 32, 8, 8192, 8192, 512,
+                                     causal=True, seed=1013),
 }
 
 

@@ -450,6 +450,33 @@ def bench_secondary(args, device, stream):
                      "roofline": roof("hbm", db / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
     del gw, kn, vn, ws
     fresh_allocations()
+    # B = 1 decode over 1K-32K keys (Hq 32, Hkv 8, d 128) with the library's
+    # split size for the shape (gqa_attention_decode_tile) and with splits of
+    # 1024; latency-bound, so timed from captured graphs (GPU time per call)
+    # and eagerly (host and launch included)
+    for skv in (1024, 4096, 16384, 32768):
+        c = workloads.DenseCase(f"decode_b1_{skv}", 1, 32, 8, 1, skv, 128, tile_s_kv=1024,
+                                decode=True, seed=1014)
+        inp = workloads.make_case(c)
+        g = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        outb = torch.empty_like(g["q"])
+        tb, _ = dense_bytes(c)
+        row = {}
+        for label, tile in (("auto", m.decode_tile(1, 8, skv)), ("tile1024", 1024)):
+            wsb = torch.empty(m.workspace_size(1, 32, 1, skv, 128, tile), dtype=torch.uint8,
+                              device=device)
+
+            def bstep(tile=tile, wsb=wsb):
+                m.decode_splitkv(g["q"], g["k"], g["v"], kv_len=g["kv_len"], scale=g["scale"],
+                                 tile_s_kv=tile, out=outb, workspace=wsb)
+            gms = time_graph(bstep, 20, 10, stream)
+            row[label] = {"tile_s_kv": tile, "us": round(gms * 1e3, 2),
+                          "eager_us": round(time_loop(bstep, 50, 20, stream) * 1e3, 2),
+                          "GB/s": round(tb / (gms * 1e-3) / 1e9, 1),
+                          "roofline_frac": round(tb / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        res[f"decode_b1_{skv}"] = row
+        del g, inp
+    fresh_allocations()
     # tiny prefill (launch-bound)
     c, _, g = setup_dense("tiny_prefill", device)
     step, out = prefill_step_fn(g, c, 0)

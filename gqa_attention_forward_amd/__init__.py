@@ -25,7 +25,8 @@ from . import _lib
 from ._lib import (GQAError, GQAInvalidArgument, GQAUnsupported,  # noqa: F401
                    GQAWorkspaceError)
 
-__all__ = ["prefill", "decode_splitkv", "decode_splitkv_noalloc", "splitkv_partial", "splitkv_merge", "paged",
+__all__ = ["prefill", "decode_splitkv", "decode_splitkv_noalloc", "decode_tile", "splitkv_partial",
+           "splitkv_merge", "paged",
            "paged_append", "workspace_size", "n_splits", "GQAError"]
 
 
@@ -106,6 +107,15 @@ def _scale(scale, d):
 
 def n_splits(Skv: int, tile_s_kv: int) -> int:
     return max(1, -(-int(Skv) // int(tile_s_kv))) if tile_s_kv > 0 else 1
+
+
+def decode_tile(B, Hkv, Skv) -> int:
+    """The library's split size for a decode of B sequences, Hkv kv heads and
+    Skv keys (about one work unit per compute unit of the current device)."""
+    out = ctypes.c_int32(0)
+    _lib.check(_lib.load().gqa_attention_decode_tile(int(B), int(Hkv), int(Skv),
+                                                     ctypes.byref(out)))
+    return int(out.value)
 
 
 def workspace_size(B, Hq, Sq, Skv, d, tile_s_kv) -> int:

@@ -66,6 +66,7 @@ SIGNATURES = {
     "gqa_attention_decode_splitkv": [_P, _STR3, _P, _STR3, _P, _STR3, _P, _STR3,
                                      _I32, _I32, _I32, _I32, _I32, _P, _F, _P, _I32,
                                      _P, ctypes.c_size_t, _P],
+    "gqa_attention_decode_tile": [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32)],
     "gqa_attention_decode_splitkv_fused": [_P, _STR3, _P, _STR3, _P, _STR3, _P, _STR3,
                                            _I32, _I32, _I32, _I32, _I32, _P, _F, _P, _I32,
                                            _P, ctypes.c_size_t, _P, _I64, _P],

@@ -331,6 +331,17 @@ gqa_status_t gqa_attention_decode_splitkv(const void* q, const int64_t q_stride[
                                workspace_bytes, stream);
 }
 
+gqa_status_t gqa_attention_decode_tile(int32_t B, int32_t Hkv, int32_t Skv, int32_t* tile_s_kv) {
+  if (!tile_s_kv) return fail(GQA_ERR_INVALID_ARGUMENT, "tile_s_kv is NULL");
+  if (B < 1 || Hkv < 1 || Skv < 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "B and Hkv must be >= 1 and Skv >= 0");
+  const int64_t cus = gqa_host::device_cus();
+  int32_t tile = 128;
+  while (tile < 8192 && (int64_t)B * Hkv * cdiv(Skv, tile) > cus) tile *= 2;
+  *tile_s_kv = tile;
+  return ok();
+}
+
 gqa_status_t gqa_attention_decode_splitkv_fused(
     const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
     const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3], int32_t B,

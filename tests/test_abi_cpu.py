@@ -60,3 +60,19 @@ def test_python_errors_map_to_exceptions():
     with pytest.raises(NotImplementedError):
         _lib.check(st)
     assert "head dim" in lib.gqa_last_error().decode()
+
+
+def test_decode_tile_rule():
+    """About one (b, kv head, split) unit per compute unit (256 on MI355X; the
+    same fallback where no device answers), powers of two from 128 to 8192."""
+    import gqa_attention_forward_amd as gqa
+    assert gqa.decode_tile(1, 8, 1024) == 128
+    assert gqa.decode_tile(1, 8, 4096) == 128
+    assert gqa.decode_tile(1, 8, 16384) == 512
+    assert gqa.decode_tile(1, 8, 32768) == 1024
+    assert gqa.decode_tile(4, 8, 4096) == 512
+    assert gqa.decode_tile(4, 8, 32768) == 4096
+    assert gqa.decode_tile(1, 8, 0) == 128
+    assert gqa.decode_tile(64, 8, 1 << 20) == 8192
+    with pytest.raises(ValueError):
+        gqa.decode_tile(0, 8, 1024)

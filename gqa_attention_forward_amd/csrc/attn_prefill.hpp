@@ -676,12 +676,13 @@ attn_prefill_kernel(const AttnArgs a) {
 
   // ---- Ping-pong of the two waves of each SIMD (8 waves, one key group,
   // d <= 128).  A wave issues in order, and an MFMA holds its wave until the
-  // matrix pipe takes it, so vector work placed between a wave's own MFMAs
-  // mostly adds to its time; vector work of ANOTHER wave on the same SIMD
-  // runs under those MFMAs for free (measured on gfx950 with register-only
-  // loops: MFMA and FMA mixed in both waves of a SIMD took the sum of their
-  // times, one wave of each took the MFMA time alone).  So each wave
-  // alternates two pure phases:
+  // matrix pipe takes it.  Measured on gfx950 (loops, one workgroup per CU):
+  // with one wave per SIMD, about two vector instructions after each MFMA
+  // run in its shadow and each further one adds ~4.5 cycles (an exponential
+  // ~8); vector work of ANOTHER wave on the SIMD costs the MFMA wave nothing,
+  // but while that wave keeps MFMAs queued the other issues only about one
+  // vector instruction per MFMA.  So each wave alternates two pure phases,
+  // and the barrier that ends a phase lets the lagging vector phase finish:
   //   M(t): S = K_t Q^T (both halves), then O += V_{t-1}^T P_{t-1}^T  (MFMA
   //         and LDS operand reads only)
   //   V(t): softmax of S_t -> P_t and the O rescale, then this thread's

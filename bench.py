@@ -292,12 +292,14 @@ def bench_cold(device, stream):
                              "roofline_frac": round(tb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del g
     c, _, g = setup_dense("shortq_longkv", device)
-    step, _ = prefill_step_fn(g, c, 2048)
-    med, mn, it = time_cold(step, stream, flush)
-    tb, _ = dense_bytes(c)
-    res["shortq_longkv_tile2048"] = {"median_ms": round(med, 5), "min_ms": round(mn, 5),
-                                     "calls": it, "GB/s": round(tb / (med * 1e-3) / 1e9, 1),
-                                     "roofline_frac": round(tb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    for tile in (2048, 4096):
+        step, _ = prefill_step_fn(g, c, tile)
+        med, mn, it = time_cold(step, stream, flush)
+        tb, _ = dense_bytes(c)
+        res[f"shortq_longkv_tile{tile}"] = {
+            "median_ms": round(med, 5), "min_ms": round(mn, 5), "calls": it,
+            "GB/s": round(tb / (med * 1e-3) / 1e9, 1),
+            "roofline_frac": round(tb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del g
     c, _, g = setup_dense("causal_prefill", device)
     step, _ = prefill_step_fn(g, c, 0)
@@ -315,9 +317,11 @@ def bench_secondary(args, device, stream):
     res = {}
     steps = max(3, min(args.steps, 20))
     fresh_allocations()
-    # short-q / long-kv prefill (HBM-bound): split-KV, 8 splits of 2048 keys
+    # short-q / long-kv prefill (HBM-bound): one pass, and split-KV with 8
+    # splits of 2048 keys (4-wave form, two workgroups per CU) or 4 of 4096
+    # (two key groups per 8-wave workgroup, one per CU)
     c, _, g = setup_dense("shortq_longkv", device)
-    for tile in (0, 2048):
+    for tile in (0, 2048, 4096):
         step, out = prefill_step_fn(g, c, tile)
         ms = time_loop(step, steps, warm_steps(step, stream), stream)
         tb, _ = dense_bytes(c)
@@ -540,7 +544,7 @@ def run_only(args, device, stream):
     if c.decode:
         step, _, _, _ = decode_step_fns(g, c)
     else:
-        step, _ = prefill_step_fn(g, c, 2048 if name == "shortq_longkv" else 0)
+        step, _ = prefill_step_fn(g, c, 4096 if name == "shortq_longkv" else 0)
     ms = time_loop(step, args.steps, args.warmup, stream)
     return {"workload": name, "ms": ms, "TFLOP/s": dense_flops(c) / (ms * 1e-3) / 1e12,
             "GB/s": dense_bytes(c)[0] / (ms * 1e-3) / 1e9}

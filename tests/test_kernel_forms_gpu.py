@@ -17,6 +17,8 @@ Family B: 128-, 256- and 512-row groups over B x Hkv = 288, at d = 64 and
 128, one pass and splits of 64 keys, dense and paged, causal.
 Head-major pools: a paged cache stored [n_pages, Hkv, 64, d] and passed by
 strides gives the token-major pool's result bit for bit.
+With the named workloads and the other GPU tests, these launch every kernel
+form the library builds (a kernel trace of the GPU suite lists them).
 """
 
 import numpy as np
@@ -108,10 +110,12 @@ def test_large_groups_wide_grid(d, Sq, layout, tile):
 
 
 # The remaining single-q-tile forms: paged one pass with 64-row groups at
-# d = 128 and 256, and a paged split at d = 32
-@pytest.mark.parametrize("d,tile", [(128, 0), (256, 0), (32, 64)])
-def test_paged_64_row_groups(d, tile):
-    run_case("paged", 6, 2, 4, 16, 300, d, tile, True, seed=400 + d)
+# d = 128 and 256, and at d = 32 a split and one pass with 64- and 128-row
+# groups (the 2- and 4-wave forms)
+@pytest.mark.parametrize("d,Sq,tile,seed", [(128, 16, 0, 528), (256, 16, 0, 656), (32, 16, 64, 432),
+                                            (32, 16, 0, 433), (32, 32, 0, 434)])
+def test_paged_64_row_groups(d, Sq, tile, seed):
+    run_case("paged", 6, 2, 4, Sq, 300, d, tile, True, seed=seed)
 
 
 # Paged splits on the 2-wave stream kernel: 32 x 4 pairs x 2 splits of 64

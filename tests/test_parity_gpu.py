@@ -100,7 +100,8 @@ def _rows(c, n, seed):
 # one pass), compared with the oracle at every output element.
 @pytest.mark.parametrize("name,tile", [("decode_splitkv", 1024), ("decode_splitkv_d256", 1024),
                                        ("decode_splitkv_d512", 1024),
-                                       ("shortq_longkv", 2048), ("shortq_longkv", 0)])
+                                       ("shortq_longkv", 2048), ("shortq_longkv", 4096),
+                                       ("shortq_longkv", 0)])
 def test_full_size_in_full(name, tile):
     c = workloads.CASES.get(name) or workloads.HEAD_DIM_CASES[name]
     note(f"{name} full size, every element, tile={tile} {c}")

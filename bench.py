@@ -439,20 +439,27 @@ def bench_secondary(args, device, stream):
     tile = 1024
     ws = torch.empty(m.workspace_size(1, w["Hq"], w["total_q"], gw["page_table"].shape[1] * 64,
                                       w["d"], tile), dtype=torch.uint8, device=device)
-    for name, append in (("paged_decode_tile1024", False), ("paged_decode_append_tile1024", True)):
-        def dstep(append=append):
+    # the same pool stored head-major ([n_pages, Hkv, 64, d]), passed by
+    # strides as the same logical view: one head's rows of a page contiguous
+    khm = gw["k_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vhm = gw["v_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    for name, append, kc, vc in (
+            ("paged_decode_tile1024", False, gw["k_cache"], gw["v_cache"]),
+            ("paged_decode_head_major_tile1024", False, khm, vhm),
+            ("paged_decode_append_tile1024", True, gw["k_cache"], gw["v_cache"])):
+        def dstep(append=append, kc=kc, vc=vc):
             if append:
-                m.paged_append(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],
+                m.paged_append(gw["q"], gw["cu_seqlens_q"], kc, vc,
                                gw["page_table"], gw["kv_len"], kn, vn, max_q_len=1,
                                scale=w["scale"], tile_s_kv=tile, out=outd, workspace=ws)
             else:
-                m.paged(gw["q"], gw["cu_seqlens_q"], gw["k_cache"], gw["v_cache"],
+                m.paged(gw["q"], gw["cu_seqlens_q"], kc, vc,
                         gw["page_table"], gw["kv_len"], max_q_len=1, scale=w["scale"],
                         tile_s_kv=tile, out=outd, workspace=ws)
         ms = time_loop(dstep, steps, warm_steps(dstep, stream), stream)
         res[name] = {"ms": round(ms, 5), "GB/s": round(db / (ms * 1e-3) / 1e9, 1),
                      "roofline": roof("hbm", db / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
-    del gw, kn, vn, ws
+    del gw, kn, vn, ws, khm, vhm
     fresh_allocations()
     # B = 1 decode over 1K-32K keys (Hq 32, Hkv 8, d 128) with the library's
     # split size for the shape (gqa_attention_decode_tile) and with splits of

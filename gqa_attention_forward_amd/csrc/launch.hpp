@@ -136,7 +136,13 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
   // d <= 64 every group of up to 64 rows, whose 32-key stream tiles carry
   // few bytes per step; at d = 128 and 256 the groups of 17-32 rows (two
   // 16-column blocks, or at d = 256 two q-tiles reading K/V twice).
-  // Paged decode at d = 128 too: its 64-key tiles are whole pages.
+  // Paged decode at d = 128 too, where one head's rows of a page are not
+  // contiguous (a token-major pool): the shared-tile form loads whole rows,
+  // the stream kernel 64-byte pieces of 16 rows per instruction, which
+  // spread over 32 KB at a 2 KB row stride.  Measured at B 16, Hkv 8, 8192
+  // keys, splits of 1024: token-major pool 91.7 us shared-tile against 97.3
+  // us stream; head-major pool 91.6 against 84.6 us, so it keeps the stream
+  // kernel.
   // Measured at B 16, Hkv 8, 8192 keys, splits of 1024: decode 52 -> 48 us
   // at d = 64; 32-row groups 112-123 -> 101-102 us at d = 128 and 382 ->
   // 219 us at d = 256; paged decode at d = 128 98-100 -> 92-95 us (dense
@@ -149,7 +155,7 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
       (int64_t)args.B * args.Hkv * args.n_split >= 2 * (int64_t)device_cus()) {
     if constexpr (D <= 64) {
       return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
-    } else if ((PAGED && D == 128 && rows <= 16) || (rows > 16 && rows <= 32)) {
+    } else if ((PAGED && D == 128 && rows <= 16 && args.kv_sr > D) || (rows > 16 && rows <= 32)) {
       if constexpr (D == 128) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
       if constexpr (D == 256) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
     }

@@ -287,6 +287,35 @@ def test_paged_append(case, causal, tile):
     assert torch.equal(vc.cpu().view(torch.int16), w["v_cache"].view(torch.int16))
 
 
+@pytest.mark.parametrize("layout", ["token-major", "head-major"])
+def test_paged_decode_full_size(layout):
+    """The timed paged decode workload (16 sequences of 8192 keys, Hq 32,
+    Hkv 8, splits of 1024), every output row against the oracle.  The
+    head-major pool ([n_pages, Hkv, 64, d] passed as the same logical view by
+    strides) takes the stream kernel, the token-major one the shared-tile
+    form."""
+    note(f"paged decode, full size, {layout} pool, tile=1024")
+    w = workloads.make_paged_decode()
+    g = to_dev(w)
+    kc, vc = g["k_cache"], g["v_cache"]
+    if layout == "head-major":
+        kc = kc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        vc = vc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        assert kc.stride(1) == w["d"]
+    out = gqa().paged(g["q"], g["cu_seqlens_q"], kc, vc, g["page_table"], g["kv_len"],
+                      max_q_len=1, scale=w["scale"], tile_s_kv=1024)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    t = np.repeat(np.arange(w["B"]), w["Hq"])
+    h = np.tile(np.arange(w["Hq"]), w["B"])
+    want = oracle.paged_attention_rows_fp64(w["q"].float().numpy(), w["cu_seqlens_q"].numpy(),
+                                            w["k_cache"].float().numpy(),
+                                            w["v_cache"].float().numpy(), w["page_table"].numpy(),
+                                            w["kv_len"].numpy(), t, h, scale=w["scale"],
+                                            page_size=64)
+    assert_close(out[t, h], want, f"paged decode full size, {layout} pool (all {t.size} rows)")
+
+
 def test_paged_append_decode_full_size():
     """The timed append workload (16 sequences of 8192 keys, Hq 32, Hkv 8,
     splits of 1024): sampled rows against the oracle over the full cache,

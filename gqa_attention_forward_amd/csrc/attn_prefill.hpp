@@ -76,6 +76,10 @@ struct PrefillCfg {
   static constexpr int TILE = BK * D;        // elements of one V tile
   static constexpr int STAGE = KTILE + TILE; // K then V
   static constexpr int LDS_BYTES = KS * 2 * STAGE * 2;
+  // The cross-tile pipelined form (4 waves, one key group, d = 256) keeps
+  // its two stages in static LDS arrays, filled by LDS DMA: no dynamic LDS.
+  static constexpr bool XP = NW == 4 && KS == 1 && D == 256;
+  static constexpr int DYN_LDS_BYTES = XP ? 0 : LDS_BYTES;
   // the launch bound's minimum waves per SIMD (it caps the registers a wave
   // may take): 2 where two sets of stages fit in 160 KiB of LDS, else 1
   // (d = 256, or two key groups at d = 128).  An 8-wave workgroup is 2 waves
@@ -92,6 +96,16 @@ struct PrefillCfg {
 constexpr float kLazyRescale = 8.f;  // log2 units
 // paged grids order their work by sequence length up to this many sequences
 constexpr int kRankedMaxB = 256;
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, expanded at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Row maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950):
 // fmaxf would first quiet each input with an extra instruction.  The scores
@@ -329,11 +343,13 @@ attn_prefill_kernel(const AttnArgs a) {
   auto tile_key = [&](int it) { return kbeg + (it * KS + kh) * BK; };
 
   Stage nx;
-  if (ntl > 0) {
-    load_tile(tile_key(0), nx, true);
-    store_tile(0, nx);
+  if constexpr (!C::XP) {
+    if (ntl > 0) {
+      load_tile(tile_key(0), nx, true);
+      store_tile(0, nx);
+    }
+    lds_barrier();
   }
-  lds_barrier();
 
   const int krow_a = swap_bits23(col);  // K row (within a 32-key half) this lane feeds to MFMA
   const int g16 = lane >> 4;
@@ -346,11 +362,14 @@ attn_prefill_kernel(const AttnArgs a) {
   // reads).  The slot swizzle of key 16 t + 8 hl + 4 half + r16 / 4 depends
   // only on the lane and `half` (key bits 0-2), so a lane needs 2 x NDB base
   // offsets and the 16-key step t is an immediate.
-  int vbase[2][NDB];
+  // The swizzle changes slot bits 1-3 only, so d blocks db and db + 4 (slot
+  // + 16) differ by a constant: bases for the first four blocks suffice.
+  constexpr int NVB = NDB < 4 ? NDB : 4;
+  int vbase[2][NVB];
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NVB; ++db) {
       const int cc = 32 * db + 16 * (g16 & 1) + 4 * (r16 & 3);
       const int key = 8 * hl + 4 * half + (r16 >> 2);
       vbase[half][db] = key * D + 8 * ((cc >> 3) ^ vslot_swz<DC>(key)) + (cc & 7);
@@ -360,7 +379,8 @@ attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half)
       va[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(Vs + vbase[half][db] + 16 * t * D));
+          (__attribute__((address_space(3))) i16x4*)(Vs + vbase[half][db % NVB] +
+                                                     128 * (db / NVB) + 16 * t * D));
     return __builtin_bit_cast(bf16x8,
                               __builtin_shufflevector(va[0], va[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
@@ -791,8 +811,244 @@ attn_prefill_kernel(const AttnArgs a) {
     }
   }
 
+  // ---- Cross-tile pipelining inside each wave (4 waves, one key group,
+  // d = 256).  One wave per SIMD, so its MFMAs can only overlap vector work
+  // of the same wave: an MFMA holds the wave until the busy matrix pipe takes
+  // it, but about two independent vector instructions after each MFMA run in
+  // its shadow, and each further one adds ~4.5 cycles (~8 for an exponential;
+  // measured on gfx950 with this MFMA stream in a loop).  A 64-key tile at
+  // d = 256 carries 64 MFMAs per wave against ~130 softmax instructions, so
+  // each wave runs the softmax of tile t between its own MFMAs of
+  // independent work, one MFMA step at a time in a fixed order, and one
+  // barrier per tile orders the stages:
+  //   steps 0 .. NA-1:   O += V_{t-1}^T P_{t-1}^T, with the mask, row max and
+  //                      lazy reference move of tile t, then its weights
+  //   steps NA .. NST-1: S_{t+1} = K_{t+1} Q^T, with the rest of the weights
+  //   then the (rare) O rescale by tile t's factor -- after the P.V of tile
+  //   t - 1, before that of tile t -- and the barrier.
+  // Both reads of an iteration come from stage (t + 1) & 1 (K of tile t + 1,
+  // V of tile t - 1).  At its start the four waves request K of tile t + 2
+  // and V of tile t into stage t & 1, whose last readers ran before the
+  // previous barrier, by LDS DMA: 64 lanes x 16 bytes straight into one
+  // 1 KiB block of the stage per instruction, with no staging registers (64
+  // per lane at d = 256) and no LDS writes in the waves.  The barrier at the
+  // iteration's end waits for them.  The stages are separate static arrays,
+  // so the compiler can tell the DMA targets from the stage the MFMA
+  // operands are read from and does not wait for the DMA there.  The first
+  // P.V has P = 0 over stage 1's V, zero-filled at the start; the last QK^T
+  // runs on an empty K tile and its S is unused.  Measured on causal
+  // prefill (B 2, Hq 32, Hkv 8, 8192 keys): 2.61 ms with the four-phase step
+  // and register staging, 2.11 ms with this one.
+  constexpr bool XP = C::XP;
+  if constexpr (XP) {
+    __shared__ __attribute__((aligned(16))) uint16_t xk0[C::KTILE], xk1[C::KTILE];
+    __shared__ __attribute__((aligned(16))) uint16_t xv0[C::TILE], xv1[C::TILE];
+    using LdsPtr = __attribute__((address_space(3))) void*;
+    static_assert(D == 256 && NW == 4, "the layouts below are for d = 256, 4 waves");
+    // K: row pairs.  One 1 KiB DMA block is a pair of 512-byte rows; pairs sit
+    // PAIR elements apart (32 bytes of pad), and the odd row of a pair holds
+    // the two 16-byte halves of each 32-byte chunk swapped.  The K operand
+    // reads (16 bytes per lane, 16 lanes over 16 rows) then hit 16 distinct
+    // 16-byte bank slots: a pair's rows differ in the half, pairs by the pad.
+    // V: rows of D elements, slot p of row r holding chunk p ^ vslot_swz(r).
+    // Wave w issues blocks i = w, w + 4, ...: a lane's row within the block
+    // and its chunk are the same in all of them (the V swizzle repeats every
+    // 8 rows), so one per-lane offset per tensor plus the block's row step.
+    // Rows past kv_len lie outside the tile's buffer and read as zeros.
+    constexpr int PAIR = 2 * D + 16;  // elements per row pair with its pad
+    static_assert(C::KTILE == 32 * PAIR, "K tile of 32 row pairs");
+    const int hi = lane >> 5;  // the block's odd row
+    const uint32_t dko = (uint32_t)hi * kss2 + 16u * (uint32_t)((lane & 31) ^ hi);
+    const uint32_t dvo =
+        (uint32_t)hi * vss2 + 16u * (uint32_t)((lane & 31) ^ vslot_swz<DC>(2 * wv + hi));
+    auto dma_k = [&](const TileRes& r, uint16_t* dst) __attribute__((always_inline)) {
+      BufRes rr = r.k;  // a const resource argument makes the host pass drop the kernel
+      for (int i = wv; i < 32; i += 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (LdsPtr)(dst + PAIR * i), 16,
+                                                 (int)(dko + 2u * (uint32_t)i * kss2), 0, 0, CP);
+    };
+    auto dma_v = [&](const TileRes& r, uint16_t* dst) __attribute__((always_inline)) {
+      BufRes rr = r.v;
+      for (int i = wv; i < 32; i += 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (LdsPtr)(dst + 512 * i), 16,
+                                                 (int)(dvo + 2u * (uint32_t)i * vss2), 0, 0, CP);
+    };
+    // K operand of d step c, key half h, in the pair layout: a per-lane base
+    // and immediates
+    const int kxo = (krow_a >> 1) * PAIR + (krow_a & 1) * D + 8 * (hl ^ (krow_a & 1));
+    auto kreadx = [&](const uint16_t* Ks, int c, int h) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(Ks + kxo + 16 * PAIR * h + 16 * c);
+    };
+    // S of the tile whose softmax runs next, P of the tile whose P.V runs
+    // next: two register sets each, which swap roles with the tile's parity
+    f32x16 sA0, sA1, sB0, sB1;
+    bf16x8 pA0[2], pA1[2], pB0[2], pB1[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) pB0[t] = pB1[t] = bf16x8{};
+    // first key of a real tile to address an empty (zero-size) load with
+    auto any_key = [&](int t) __attribute__((always_inline)) {
+      return tile_key(max(0, min(t, ntl - 1)));
+    };
+    auto xp_step = [&](auto mask_tag, int t, auto par, const f32x16& sc0, const f32x16& sc1,
+                       f32x16& sn0, f32x16& sn1, const bf16x8 (&pv0)[2], const bf16x8 (&pv1)[2],
+                       bf16x8 (&pc0)[2], bf16x8 (&pc1)[2]) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par)::value;
+      constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr int PD = 3;          // operand reads run this many MFMAs ahead
+      constexpr int NA = 4 * NDB;    // P.V MFMAs
+      constexpr int NB = 2 * NCK;    // K Q^T MFMAs
+      constexpr int NST = NA + NB;   // all MFMA steps of the iteration
+      const uint16_t* Kn = PAR ? xk0 : xk1;  // K of tile t + 1
+      const uint16_t* Vp = PAR ? xv0 : xv1;  // V of tile t - 1
+      dma_k(tile_res(any_key(t + 2), t + 2 < ntl), PAR ? xk1 : xk0);
+      dma_v(tile_res(tile_key(t), true), PAR ? xv1 : xv0);
+      // operand of MFMA step g: V^T of P.V step g, then K of K Q^T step g - NA
+      auto opread = [&](int g) __attribute__((always_inline)) {
+        return g < NA ? vread(Vp, g / NDB, g % NDB) : kreadx(Kn, (g - NA) >> 1, (g - NA) & 1);
+      };
+      f32x16 c0 = sc0, c1 = sc1;
+      const int rem1 = lim - tile_key(t) - 8 * hl - 1;  // masked key offsets: o > rem1
+      float m = -INFINITY, mx = 0.f, alpha = 1.f, mu = 0.f, ls = 0.f;
+      u32x4 w[2][2];  // packed weights: key half, 16-key group
+      sn0 = f32x16{};
+      sn1 = f32x16{};
+      bf16x8 ob[PD + 1];
+#pragma unroll
+      for (int g = 0; g < PD; ++g) ob[g] = opread(g);
+      __builtin_amdgcn_sched_barrier(0);
+      // One MFMA per step, the read PD steps ahead, and a fixed share of the
+      // softmax of tile t: steps 0-3 mask (tiles that need it) and take the
+      // row max over 4 of the 16 register pairs each, step 4 the reference
+      // move, then the 16 weight pairs spread over the remaining steps.
+      // (expanded at compile time: a 64-step loop at d = 256 is too large
+      // for the unroller, and a rolled loop indexes the register arrays)
+      auto mstep = [&](auto gc) __attribute__((always_inline)) {
+        constexpr int g = decltype(gc)::value;
+        if constexpr (g < NA) {
+          constexpr int i = g;
+          const bf16x8& pb = (i / NDB) & 1 ? ((i / NDB) >> 1 ? pv1[1] : pv0[1])
+                                            : ((i / NDB) >> 1 ? pv1[0] : pv0[0]);
+          acc[i % NDB] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[g % (PD + 1)], pb, acc[i % NDB], 0, 0, 0);
+        } else {
+          constexpr int i = g - NA;
+          if constexpr (i & 1)
+            sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[g % (PD + 1)], qf[i >> 1], sn1, 0, 0, 0);
+          else
+            sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob[g % (PD + 1)], qf[i >> 1], sn0, 0, 0, 0);
+        }
+        if constexpr (g + PD < NST) ob[(g + PD) % (PD + 1)] = opread(g + PD);
+        if constexpr (g < 4) {
+#pragma unroll
+          for (int j = 4 * g; j < 4 * g + 4; ++j) {
+            if constexpr (MASK) {
+              // the sign of rem1 - o is an all-ones word for a masked
+              // offset o, merged bitwise (no compare masks to hold)
+              constexpr uint32_t kNegInf = 0xff800000u;
+              const uint32_t m0 = (uint32_t)((rem1 - (16 * (j >> 3) + (j & 7))) >> 31);
+              const uint32_t m1 = (uint32_t)((rem1 - (32 + 16 * (j >> 3) + (j & 7))) >> 31);
+              c0[j] = __uint_as_float((m0 & kNegInf) | (~m0 & __float_as_uint(c0[j])));
+              c1[j] = __uint_as_float((m1 & kNegInf) | (~m1 & __float_as_uint(c1[j])));
+            }
+            m = vmax(vmax(m, c0[j]), c1[j]);
+          }
+          if constexpr (g == 3) mx = half_swap_max(m) * a.scale_log2;
+        } else if constexpr (g == 4) {
+          mtrue = fmaxf(mtrue, mx);
+          const bool move = mx > mref + kLazyRescale;
+          alpha = move ? ex2(mref - mx) : 1.f;  // 0 when mref = -inf
+          mref = move ? mx : mref;
+          mu = (mref == -INFINITY) ? 0.f : mref;
+        } else {
+          // weight pair k (two adjacent keys of one row) at step 5 + k (NST - 5) / 16:
+          // rounded once to bf16x2, which feeds both the row sum and P
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            if (5 + k * (NST - 5) / 16 != g) continue;
+            const int hf = k >> 3, grp = (k >> 2) & 1, e = k & 3;
+            const f32x16& sv = hf ? c1 : c0;
+            const f32x2 x = {ex2(__builtin_fmaf(sv[8 * grp + 2 * e], a.scale_log2, -mu)),
+                             ex2(__builtin_fmaf(sv[8 * grp + 2 * e + 1], a.scale_log2, -mu))};
+            const bf16x2 pp = __builtin_convertvector(x, bf16x2);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
+            w[hf][grp][e] = __builtin_bit_cast(uint32_t, pp);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      static_for<NST>(mstep);
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp) {
+        pc0[grp] = __builtin_bit_cast(bf16x8, w[0][grp]);
+        pc1[grp] = __builtin_bit_cast(bf16x8, w[1][grp]);
+      }
+      l = l * alpha + ls;
+      // keeps the softmax in the MFMA steps above: left free, the compiler
+      // sinks the exponentials past the rescale branch, out of the shadows
+      pin(pc0);
+      pin(pc1);
+      asm volatile("" ::"v"(l));
+      rescale(alpha);
+      lds_barrier();  // also waits for this wave's DMA
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // tile t of parity 0 takes S from set A and P of tile t - 1 from set B
+    auto xp0 = [&](auto mask_tag, int t) __attribute__((always_inline)) {
+      xp_step(mask_tag, t, P0{}, sA0, sA1, sB0, sB1, pB0, pB1, pA0, pA1);
+    };
+    auto xp1 = [&](auto mask_tag, int t) __attribute__((always_inline)) {
+      xp_step(mask_tag, t, P1{}, sB0, sB1, sA0, sA1, pA0, pA1, pB0, pB1);
+    };
+    if (ntl > 0) {
+      // stage 0: tile 0; stage 1: K of tile 1, V zeros (0 x inf would be NaN)
+      {
+        const TileRes r0 = tile_res(tile_key(0), true);
+        dma_k(r0, xk0);
+        dma_v(r0, xv0);
+        dma_k(tile_res(any_key(1), ntl > 1), xk1);
+      }
+#pragma unroll
+      for (int i = 0; i < C::TILE / (8 * C::NT); ++i)
+        *reinterpret_cast<u32x4*>(xv1 + 8 * (tid + i * C::NT)) = u32x4{};
+      lds_barrier();
+      // S of tile 0
+      sA0 = f32x16{};
+      sA1 = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        sA0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreadx(xk0, c, 0), qf[c], sA0, 0, 0, 0);
+        sA1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreadx(xk0, c, 1), qf[c], sA1, 0, 0, 0);
+      }
+      lds_barrier();       // read by every wave before iteration 0 refills stage 0
+      int u = 0;
+      for (; u + 1 < nfull; u += 2) {
+        xp0(False{}, u);
+        xp1(False{}, u + 1);
+      }
+      if (u < nfull) {  // odd number of unmasked tiles
+        xp0(False{}, u);
+        ++u;
+        if (u < ntl) {
+          xp1(True{}, u);
+          ++u;
+        }
+      }
+      for (; u + 1 < ntl; u += 2) {
+        xp0(True{}, u);
+        xp1(True{}, u + 1);
+      }
+      if (u < ntl) xp0(True{}, u);
+      // O += V^T P^T of the last tile
+      if ((ntl - 1) & 1)
+        pv2(xv1, pB0, pB1);
+      else
+        pv2(xv0, pA0, pA1);
+    }
+  }
+
   int it = 0;
-  if constexpr (PP) {
+  if constexpr (PP || XP) {
     // done above
   } else if constexpr (EARLY) {
     // Tiles two at a time (stages 0 and 1), unmasked tiles first, then the

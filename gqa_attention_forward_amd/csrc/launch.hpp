@@ -67,10 +67,10 @@ gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream
   args.spw = 1;
   if constexpr (KS == 1 || D == 128)
     if (cdiv(rows, C::ROWS) == 1)
-      return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS, true>, C::LDS_BYTES,
+      return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS, true>, C::DYN_LDS_BYTES,
                          C::NT, args, rows, C::ROWS, stream);
   if constexpr (NW == 8 || (NW == 4 && (D == 32 || D == 256)))
-    return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS, false>, C::LDS_BYTES,
+    return launch_grid(&gqa::attn_prefill_kernel<D, NW, PAGED, PARTIAL, KS, false>, C::DYN_LDS_BYTES,
                        C::NT, args, rows, C::ROWS, stream);
   return fail(GQA_ERR_UNSUPPORTED, "no prefill form for %lld rows at d = %d, %d waves",
               (long long)rows, D, NW);

@@ -156,20 +156,30 @@ gqa_status_t launch_merge(const void* workspace, void* o, const int64_t* os, int
   const float2* ml = reinterpret_cast<const float2*>(workspace);
   const float* ot = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
                                                    (size_t)rows * n_split * 8);
-  const int64_t nblocks = cdiv(rows, 4);
+  // d = 128 merges with fewer rows than 8 per CU (decode) keep one row per
+  // wave; larger ones and the other head dims take the packed form
+  const bool one_row = d == 128 && rows < 8 * (int64_t)gqa_host::device_cus();
+  using gqa::kMergePackedLpr;
+  const int rpb = d == 32    ? gqa::MergeCfg<32, kMergePackedLpr<32>>::ROWS_PER_BLOCK
+                  : d == 64  ? gqa::MergeCfg<64, kMergePackedLpr<64>>::ROWS_PER_BLOCK
+                  : d == 128 ? (one_row ? gqa::MergeCfg<128, 64>::ROWS_PER_BLOCK
+                                        : gqa::MergeCfg<128, kMergePackedLpr<128>>::ROWS_PER_BLOCK)
+                  : d == 256 ? gqa::MergeCfg<256, kMergePackedLpr<256>>::ROWS_PER_BLOCK
+                             : gqa::MergeCfg<512, kMergePackedLpr<512>>::ROWS_PER_BLOCK;
+  const int64_t nblocks = cdiv(rows, rpb);
   if (nblocks * 256 > 0xffffffffLL)  // work-items of one dispatch: 32 bits
     return fail(GQA_ERR_UNSUPPORTED, "merge grid too large (%lld rows)", (long long)rows);
   (void)hipGetLastError();
-  auto kern = sparse ? (d == 32 ? gqa::merge_kernel<32, true>
-                        : d == 64 ? gqa::merge_kernel<64, true>
-                        : d == 128 ? gqa::merge_kernel<128, true>
-                        : d == 256 ? gqa::merge_kernel<256, true>
-                                   : gqa::merge_kernel<512, true>)
-                     : (d == 32 ? gqa::merge_kernel<32, false>
-                        : d == 64 ? gqa::merge_kernel<64, false>
-                        : d == 128 ? gqa::merge_kernel<128, false>
-                        : d == 256 ? gqa::merge_kernel<256, false>
-                                   : gqa::merge_kernel<512, false>);
+  auto pick = [&](auto sp) {
+    constexpr bool S = decltype(sp)::value;
+    return d == 32    ? gqa::merge_kernel<32, S, kMergePackedLpr<32>>
+           : d == 64  ? gqa::merge_kernel<64, S, kMergePackedLpr<64>>
+           : d == 128 ? (one_row ? gqa::merge_kernel<128, S, 64>
+                                 : gqa::merge_kernel<128, S, kMergePackedLpr<128>>)
+           : d == 256 ? gqa::merge_kernel<256, S, kMergePackedLpr<256>>
+                      : gqa::merge_kernel<512, S, kMergePackedLpr<512>>;
+  };
+  auto kern = sparse ? pick(std::true_type{}) : pick(std::false_type{});
   hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(256), 0, stream, ml, ot,
                      reinterpret_cast<uint16_t*>(o), os[0], os[1], os[2], sink, Hq, Sq, n_split,
                      rows);

@@ -266,6 +266,17 @@ def bench_decode(args, device, stream):
     }
 
 
+def paged_head_major(w, device):
+    """The paged decode workload's tensors on `device`, with its K/V pools
+    stored head-major ([n_pages, Hkv, 64, d], laid out on the host) and
+    returned as the same logical [n_pages, 64, Hkv, d] views."""
+    gw = {k: (v.to(device) if isinstance(v, torch.Tensor) and k not in ("k_cache", "v_cache")
+              else v) for k, v in w.items()}
+    khm = w["k_cache"].permute(0, 2, 1, 3).contiguous().to(device).permute(0, 2, 1, 3)
+    vhm = w["v_cache"].permute(0, 2, 1, 3).contiguous().to(device).permute(0, 2, 1, 3)
+    return gw, khm, vhm
+
+
 def fresh_allocations():
     """Release the blocks the caching allocator kept from earlier workloads,
     so that the next workload's tensors are new device allocations, as in a
@@ -439,13 +450,8 @@ def bench_secondary(args, device, stream):
     tile = 1024
     ws = torch.empty(m.workspace_size(1, w["Hq"], w["total_q"], gw["page_table"].shape[1] * 64,
                                       w["d"], tile), dtype=torch.uint8, device=device)
-    # the same pool stored head-major ([n_pages, Hkv, 64, d]), passed by
-    # strides as the same logical view: one head's rows of a page contiguous
-    khm = gw["k_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
-    vhm = gw["v_cache"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     for name, append, kc, vc in (
             ("paged_decode_tile1024", False, gw["k_cache"], gw["v_cache"]),
-            ("paged_decode_head_major_tile1024", False, khm, vhm),
             ("paged_decode_append_tile1024", True, gw["k_cache"], gw["v_cache"])):
         def dstep(append=append, kc=kc, vc=vc):
             if append:
@@ -459,7 +465,24 @@ def bench_secondary(args, device, stream):
         ms = time_loop(dstep, steps, warm_steps(dstep, stream), stream)
         res[name] = {"ms": round(ms, 5), "GB/s": round(db / (ms * 1e-3) / 1e9, 1),
                      "roofline": roof("hbm", db / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
-    del gw, kn, vn, ws, khm, vhm
+    del gw, kn, vn, ws
+    fresh_allocations()
+    # the same pool stored head-major ([n_pages, Hkv, 64, d]) and passed by
+    # strides as the same logical view (one head's rows of a page contiguous),
+    # in fresh allocations of its own
+    gw, khm, vhm = paged_head_major(w, device)
+    ws = torch.empty(m.workspace_size(1, w["Hq"], w["total_q"], gw["page_table"].shape[1] * 64,
+                                      w["d"], tile), dtype=torch.uint8, device=device)
+    outd = torch.empty_like(gw["q"])
+
+    def hstep():
+        m.paged(gw["q"], gw["cu_seqlens_q"], khm, vhm, gw["page_table"], gw["kv_len"],
+                max_q_len=1, scale=w["scale"], tile_s_kv=tile, out=outd, workspace=ws)
+    ms = time_loop(hstep, steps, warm_steps(hstep, stream), stream)
+    res["paged_decode_head_major_tile1024"] = {
+        "ms": round(ms, 5), "GB/s": round(db / (ms * 1e-3) / 1e9, 1),
+        "roofline": roof("hbm", db / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+    del gw, khm, vhm, ws, outd
     fresh_allocations()
     # B = 1 decode over 1K-32K keys (Hq 32, Hkv 8, d 128) with the library's
     # split size for the shape (gqa_attention_decode_tile) and with splits of
@@ -521,6 +544,15 @@ def run_only(args, device, stream):
                              gw["page_table"], gw["kv_len"], max_q_len=w["max_q_len"],
                              scale=w["scale"], sink=gw["sink"], tile_s_kv=tile)
         return {"workload": name, "ms": time_loop(fn, args.steps, args.warmup, stream)}
+    if name == "paged_decode_head_major":
+        w = workloads.make_paged_decode()
+        gw, khm, vhm = paged_head_major(w, device)
+        m = gqa()
+        fn = lambda: m.paged(gw["q"], gw["cu_seqlens_q"], khm, vhm,  # noqa: E731
+                             gw["page_table"], gw["kv_len"], max_q_len=1, scale=w["scale"],
+                             tile_s_kv=1024)
+        ms = time_loop(fn, args.steps, args.warmup, stream)
+        return {"workload": name, "ms": ms, "GB/s": paged_work(w)[0] / (ms * 1e-3) / 1e9}
     if name in ("paged_decode", "paged_decode_append"):
         w = workloads.make_paged_decode()
         kn, vn, _, _ = workloads.take_new_kv(w)
@@ -686,7 +718,7 @@ def main():
     ap.add_argument("--only", choices=["decode_partial", "shortq_longkv", "causal_prefill",
                                        "ragged_paged", "ragged_paged_onepass",
                                        "paged_causal_chunked", "paged_decode",
-                                       "paged_decode_append", "copy",
+                                       "paged_decode_head_major", "paged_decode_append", "copy",
                                        *workloads.HEAD_DIM_CASES],
                     help="profiling aid: time only this workload's kernels and print its line")
     args = ap.parse_args()

@@ -35,13 +35,18 @@
 //                         keys of one d).
 //   16-byte V slots in LDS are XOR-swizzled per row (vslot_swz), which makes
 //   both the b128 row writes and the transposing reads bank-conflict free.
+//   KROW (paged pools stored token-major, d = 128): K is loaded like V, as
+//   whole rows (four 256-byte rows per instruction rather than 64-byte
+//   pieces of 16 rows spread over the 2 KB row stride), written to a
+//   wave-private LDS tile with rows padded by 16 bytes and read back in the
+//   A layout above; it reaches the MFMAs bit for bit as the direct form's.
 #pragma once
 
 #include "common.hpp"
 
 namespace gqa {
 
-template <int D, int NQB>
+template <int D, int NQB, bool KROW = false>
 struct StreamCfg {
   static constexpr int BK = 32;             // keys per tile
   static constexpr int NC = D / 32;         // 32-wide d steps of Q.K
@@ -49,6 +54,11 @@ struct StreamCfg {
   static constexpr int DC = D / 8;          // 16-byte chunks per row
   static constexpr int VPL = BK * DC / 64;  // V chunks per lane per tile
   static constexpr int VTILE = BK * D;      // V tile elements (per wave)
+  // K as whole rows (KROW): a wave-private K tile, rows padded by 16 bytes
+  // so that the operand reads (16 rows, one 16-byte slot each) and the row
+  // writes are bank-conflict free
+  static constexpr int KP = D + 8;
+  static constexpr int KTILE = KROW ? BK * KP : 0;
   static constexpr int SLOT_F = NQB * (2 + 4 * NDB) * 64;  // combine floats per wave
   static constexpr int PSTR = D + 4;       // parked column: O (D floats), m, l, pad
   static constexpr int PEND_F = NQB * 16 * PSTR;  // parked floats per split
@@ -59,7 +69,7 @@ struct StreamCfg {
   // LDS: one V tile per wave, one combine slot per wave other than 0,
   // (partial mode) one parked state per split of the run, and Q at d = 256
   static constexpr int lds_bytes(int nw, int spw) {
-    return nw * VTILE * 2 + (nw - 1) * SLOT_F * 4 + spw * PEND_F * 4 + QTILE * 2;
+    return nw * (VTILE + KTILE) * 2 + (nw - 1) * SLOT_F * 4 + spw * PEND_F * 4 + QTILE * 2;
   }
   static constexpr int LDS_LIMIT = 160 * 1024;
   // splits per workgroup: up to 8 (one 16-column block) or 4, as LDS allows
@@ -79,10 +89,10 @@ struct StreamCfg {
 // few, long-running waves per CU anyway.
 // NT: no other workgroup reads this one's K/V tiles (one q-tile), which
 // are then loaded with the non-temporal hint.
-template <int D, int NQB, int NW, bool PAGED, bool PARTIAL, bool NT>
+template <int D, int NQB, int NW, bool PAGED, bool PARTIAL, bool NT, bool KROW = false>
 __global__ void __launch_bounds__(NW * 64, 1)
 attn_stream_kernel(const AttnArgs a) {
-  using C = StreamCfg<D, NQB>;
+  using C = StreamCfg<D, NQB, KROW>;
   constexpr int CP = NT ? kCpNonTemporal : kCpDefault;
   // tiles in flight per wave while it computes on one.  Two at d = 128 with
   // one 16-column block (the decode form): the split-KV decode's partial
@@ -101,6 +111,8 @@ attn_stream_kernel(const AttnArgs a) {
   constexpr int NDB = C::NDB;
   constexpr int DC = C::DC;
   constexpr int VPL = C::VPL;
+  // whole-row K loads with V in `load` (the early-issue order)
+  static_assert(!KROW || (!LATE && 2 * NC == VPL), "whole-row K: one K load per V load");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int lane = threadIdx.x & 63;
@@ -179,7 +191,7 @@ attn_stream_kernel(const AttnArgs a) {
   }
 
   // d = 256: Q goes to LDS once (wave 0 writes, every wave reads it per tile)
-  uint16_t* qlds = smem + NW * C::VTILE + 2 * ((NW - 1) * C::SLOT_F) +
+  uint16_t* qlds = smem + NW * (C::VTILE + C::KTILE) + 2 * ((NW - 1) * C::SLOT_F) +
                    2 * (PARTIAL ? a.spw * C::PEND_F : 0);
   if constexpr (C::Q_LDS) {
     if (wv == 0) {
@@ -231,6 +243,10 @@ attn_stream_kernel(const AttnArgs a) {
   for (int kb = 0; kb < 2; ++kb) koff[kb] = (uint32_t)(16 * kb + c16) * kss2 + 16u * grp;
   const uint32_t voff = (uint32_t)(lane / DC) * vss2 + 16u * (lane % DC);
   const uint32_t vstep = (uint32_t)(64 / DC) * vss2;
+  // whole-row K: chunk j of the lane is row lane / DC + j (64 / DC), 16-byte
+  // slot lane % DC (the V pattern), kept in t.k[j / NC][j % NC]
+  const uint32_t kroff = (uint32_t)(lane / DC) * kss2 + 16u * (lane % DC);
+  const uint32_t krstep = (uint32_t)(64 / DC) * kss2;
   // page table through the constant address space: uniform reads become
   // scalar loads, which do not queue behind the tile loads in flight
   const __attribute__((address_space(4))) int32_t* ptab =
@@ -255,11 +271,17 @@ attn_stream_kernel(const AttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) t.k[kb][c] = buf_load16<CP>(kr, koff[kb] + 64u * c);
+      for (int c = 0; c < NC; ++c) {
+        if constexpr (KROW)
+          t.k[kb][c] = buf_load16<CP>(kr, kroff + (uint32_t)(kb * NC + c) * krstep);
+        else
+          t.k[kb][c] = buf_load16<CP>(kr, koff[kb] + 64u * c);
+      }
 #pragma unroll
     for (int j = 0; j < VPL; ++j) t.v[j] = buf_load16<CP>(vr, voff + (uint32_t)j * vstep);
   };
   // the K (which = 0) or V (which = 1) half of `load`, for the late-issue order
+  // (operand-shaped K only)
   auto tile_res = [&](int j0, int which, bool live) {
     const uint16_t* p;
     if constexpr (PAGED) {
@@ -287,7 +309,8 @@ attn_stream_kernel(const AttnArgs a) {
   };
 
   uint16_t* vbuf = smem + wv * C::VTILE;
-  float* slots = reinterpret_cast<float*>(smem + NW * C::VTILE);
+  uint16_t* kbuf = smem + NW * C::VTILE + wv * C::KTILE;
+  float* slots = reinterpret_cast<float*>(smem + NW * (C::VTILE + C::KTILE));
   float* pend = slots + (NW - 1) * C::SLOT_F;  // parked split states (partial mode)
 
   // At d = 256 the swizzle repeats every 8 key rows: V row writes need 4
@@ -324,7 +347,16 @@ attn_stream_kernel(const AttnArgs a) {
       }
     }
   };
-  // S^T = K Q^T for two 16-key blocks
+  // whole-row K tile -> wave-private LDS (row-major, padded rows)
+  const int kwo = (lane / DC) * C::KP + 8 * (lane % DC);
+  const int kro = c16 * C::KP + 8 * grp;
+  auto stage_k = [&](const Tile& t) {
+#pragma unroll
+    for (int j = 0; j < 2 * NC; ++j)
+      *reinterpret_cast<uint4*>(kbuf + kwo + j * (64 / DC) * C::KP) = t.k[j / NC][j % NC];
+  };
+  // S^T = K Q^T for two 16-key blocks; the A operand (key row 16 kb + c16,
+  // d 32 c + 8 grp .. + 7) from the registers, or read back from the K tile
   auto qk = [&](const Tile& t, f32x4 (&s)[NQB][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -332,9 +364,14 @@ attn_stream_kernel(const AttnArgs a) {
       for (int qb = 0; qb < NQB; ++qb) {
         s[qb][kb] = f32x4{};
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, t.k[kb][c]), qop(qb, c), s[qb][kb], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) {
+          bf16x8 ka;
+          if constexpr (KROW)
+            ka = *reinterpret_cast<const bf16x8*>(kbuf + kro + 16 * kb * C::KP + 32 * c);
+          else
+            ka = __builtin_bit_cast(bf16x8, t.k[kb][c]);
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop(qb, c), s[qb][kb], 0, 0, 0);
+        }
       }
   };
   // mask, online softmax and O^T += V^T P^T of the tile at key j0
@@ -538,6 +575,7 @@ attn_stream_kernel(const AttnArgs a) {
             // keep the prefetch ahead of the first wait on tile k + u
             __builtin_amdgcn_sched_barrier(0);
             stage_v(t[u]);
+            if constexpr (KROW) stage_k(t[u]);
             compute(tile_key(k + u), t[u]);
           } else {
             // next V once this V is in LDS, next K once this K has been used
@@ -579,8 +617,14 @@ attn_stream_kernel(const AttnArgs a) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-              tn.k[kb][c] = buf_load16<CP>(kr, (uint32_t)(16 * kb + c16) * ns2 + 64u * c + 16u * grp);
+            for (int c = 0; c < NC; ++c) {
+              if constexpr (KROW)
+                tn.k[kb][c] = buf_load16<CP>(
+                    kr, (uint32_t)(lane / DC + (kb * NC + c) * (64 / DC)) * ns2 + 16u * (lane % DC));
+              else
+                tn.k[kb][c] =
+                    buf_load16<CP>(kr, (uint32_t)(16 * kb + c16) * ns2 + 64u * c + 16u * grp);
+            }
 #pragma unroll
           for (int j = 0; j < VPL; ++j)
             tn.v[j] = buf_load16<CP>(vr, (uint32_t)(lane / DC + j * (64 / DC)) * ns2 +
@@ -592,6 +636,7 @@ attn_stream_kernel(const AttnArgs a) {
           for (int qb = 0; qb < NQB; ++qb)
             lim[qb] = a.causal ? min(max(n - q_len + pq[qb] + 1, 0), n) : n;
           stage_v(tn);
+          if constexpr (KROW) stage_k(tn);
           compute(nl, tn);
         }
         if (qt == 0) {

@@ -79,14 +79,14 @@ gqa_status_t launch_prefill(gqa::AttnArgs args, int64_t rows, hipStream_t stream
 
 // The non-temporal form where one q-tile covers the group's rows; only 17-32
 // rows at d = 256 (one 16-column block per q-tile) take two.
-template <int D, int NQB, int NW, bool PAGED, bool PARTIAL>
+template <int D, int NQB, int NW, bool PAGED, bool PARTIAL, bool KROW = false>
 gqa_status_t launch_stream_nw(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  using C = gqa::StreamCfg<D, NQB>;
+  using C = gqa::StreamCfg<D, NQB, KROW>;
   const int lds = C::lds_bytes(NW, PARTIAL ? args.spw : 0);
   const int lds_max = C::lds_bytes(NW, PARTIAL ? C::max_spw(NW) : 0);
   if (cdiv(rows, 16 * NQB) == 1)
-    return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL, true>, lds, NW * 64,
-                       args, rows, 16 * NQB, stream, lds_max);
+    return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL, true, KROW>, lds,
+                       NW * 64, args, rows, 16 * NQB, stream, lds_max);
   if constexpr (D == 256 && NQB == 1)
     return launch_grid(&gqa::attn_stream_kernel<D, NQB, NW, PAGED, PARTIAL, false>, lds, NW * 64,
                        args, rows, 16 * NQB, stream, lds_max);
@@ -101,9 +101,9 @@ gqa_status_t launch_stream_nw(gqa::AttnArgs args, int64_t rows, hipStream_t stre
 // many workgroups as CUs (the same decode: 2 waves per workgroup beat 4);
 // four when the grid is smaller, to use more of each CU (where the four
 // waves' combine slots fit in LDS: not for 32-row groups at d = 256).
-template <int D, int NQB, bool PAGED, bool PARTIAL>
+template <int D, int NQB, bool PAGED, bool PARTIAL, bool KROW = false>
 gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream) {
-  using C = gqa::StreamCfg<D, NQB>;
+  using C = gqa::StreamCfg<D, NQB, KROW>;
   const int64_t cus = device_cus();
   const int64_t per_split = (int64_t)args.B * args.Hkv * cdiv(rows, 16 * NQB);
   int spw = 1;
@@ -114,8 +114,8 @@ gqa_status_t launch_stream(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
   args.spw = spw;
   const int64_t nblocks = per_split * cdiv(args.n_split, spw);
   if constexpr (C::FOUR_WAVES)
-    if (nblocks < cus) return launch_stream_nw<D, NQB, 4, PAGED, PARTIAL>(args, rows, stream);
-  return launch_stream_nw<D, NQB, 2, PAGED, PARTIAL>(args, rows, stream);
+    if (nblocks < cus) return launch_stream_nw<D, NQB, 4, PAGED, PARTIAL, KROW>(args, rows, stream);
+  return launch_stream_nw<D, NQB, 2, PAGED, PARTIAL, KROW>(args, rows, stream);
 }
 
 // Kernel choice by query rows per (b, kv head) and grid size.  Groups of up
@@ -136,18 +136,11 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
   // d <= 64 every group of up to 64 rows, whose 32-key stream tiles carry
   // few bytes per step; at d = 128 and 256 the groups of 17-32 rows (two
   // 16-column blocks, or at d = 256 two q-tiles reading K/V twice).
-  // Paged decode at d = 128 too, where one head's rows of a page are not
-  // contiguous (a token-major pool): the shared-tile form loads whole rows,
-  // the stream kernel 64-byte pieces of 16 rows per instruction, which
-  // spread over 32 KB at a 2 KB row stride.  Measured at B 16, Hkv 8, 8192
-  // keys, splits of 1024: token-major pool 91.7 us shared-tile against 97.3
-  // us stream; head-major pool 91.6 against 84.6 us, so it keeps the stream
-  // kernel.
   // Measured at B 16, Hkv 8, 8192 keys, splits of 1024: decode 52 -> 48 us
   // at d = 64; 32-row groups 112-123 -> 101-102 us at d = 128 and 382 ->
-  // 219 us at d = 256; paged decode at d = 128 98-100 -> 92-95 us (dense
-  // decode there stays faster on the stream kernel, 82 against 88 us, and
-  // so does paged decode at d = 256, 173 against 198 us).  Smaller grids
+  // 219 us at d = 256 (dense decode at d = 128 stays faster on the stream
+  // kernel, 82 against 88 us, and so does paged decode at d = 256, 173
+  // against 198 us).  Smaller grids
   // keep the stream kernel, whose launch shape adapts to them (B 1 decode
   // at d = 64: 18 us, 24 us routed).  The fused append and the in-kernel
   // merge live in the stream kernel only.
@@ -155,11 +148,23 @@ gqa_status_t dispatch_rows(gqa::AttnArgs args, int64_t rows, hipStream_t stream)
       (int64_t)args.B * args.Hkv * args.n_split >= 2 * (int64_t)device_cus()) {
     if constexpr (D <= 64) {
       return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
-    } else if ((PAGED && D == 128 && rows <= 16 && args.kv_sr > D) || (rows > 16 && rows <= 32)) {
+    } else if (rows > 16 && rows <= 32) {
       if constexpr (D == 128) return launch_prefill<D, 2, PAGED, PARTIAL>(args, rows, stream);
       if constexpr (D == 256) return launch_prefill<D, 4, PAGED, PARTIAL>(args, rows, stream);
     }
   }
+  // Paged groups of up to 16 rows at d = 128 whose pool is token-major (one
+  // head's rows of a page 2 KB or more apart): the stream kernel with K
+  // loaded as whole rows and staged through LDS.  Its operand-shaped K loads
+  // (64-byte pieces of 16 rows per instruction) spread over 32 KB there.
+  // Measured at B 16, Hkv 8, 8192 keys, splits of 1024: 96-97 us with
+  // operand-shaped K, 91.7 us on the shared-tile form, 90-91 us with whole
+  // rows; a pure load loop over the same pool reads it in 89.2 us with the
+  // operand shape and 80.5 us with whole rows.  Head-major pools keep the
+  // operand shape (84.6 us; whole rows 80.0 against 77.7 us in the loop).
+  if constexpr (PAGED && D == 128)
+    if (rows <= 16 && args.kv_sr > D)
+      return launch_stream<D, 1, PAGED, PARTIAL, true>(args, rows, stream);
   if (rows <= 16) return launch_stream<D, 1, PAGED, PARTIAL>(args, rows, stream);
   if (rows <= 32) {
     // two 16-column blocks of Q do not fit beside the d = 256 tiles: two q-tiles

@@ -16,7 +16,9 @@ B x Hkv = 256, one pass and one split of 64 keys, dense and paged.
 Family B: 128-, 256- and 512-row groups over B x Hkv = 288, at d = 64 and
 128, one pass and splits of 64 keys, dense and paged, causal.
 Head-major pools: a paged cache stored [n_pages, Hkv, 64, d] and passed by
-strides gives the token-major pool's result bit for bit.
+strides gives the token-major pool's result bit for bit (at d = 128 and up
+to 16 rows the two pools take the stream kernel's two K load forms: whole
+rows staged through LDS, and straight into the MFMA operand).
 With the named workloads and the other GPU tests, these launch every kernel
 form the library builds (a kernel trace of the GPU suite lists them).
 """
@@ -125,6 +127,15 @@ def test_paged_64_row_groups(d, Sq, tile, seed):
 @pytest.mark.parametrize("Sq", [1, 8])
 def test_paged_split_stream_wide_grid(d, Sq):
     run_case("paged", 32, 4, 4, Sq, 128, d, 64, Sq > 1, seed=500 + d + Sq)
+
+
+# Paged pools with one kv head (row stride d, so the stream kernel loads K
+# in MFMA operand shape) over 256 sequences: the 2-wave stream forms, one
+# pass and splits of 64 keys (token-major pools with several kv heads take
+# the whole-row K forms instead)
+@pytest.mark.parametrize("tile", [0, 64])
+def test_paged_one_head_wide_grid(tile):
+    run_case("paged", 256, 1, 4, 1, 128, 128, tile, False, seed=700 + tile)
 
 
 # The pool stored head-major ([n_pages, Hkv, 64, d]) and passed through the

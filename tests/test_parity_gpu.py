@@ -292,8 +292,8 @@ def test_paged_decode_full_size(layout):
     """The timed paged decode workload (16 sequences of 8192 keys, Hq 32,
     Hkv 8, splits of 1024), every output row against the oracle.  The
     head-major pool ([n_pages, Hkv, 64, d] passed as the same logical view by
-    strides) takes the stream kernel, the token-major one the shared-tile
-    form."""
+    strides) takes the stream kernel with K in MFMA operand form, the
+    token-major one the stream kernel with K loaded as whole rows."""
     note(f"paged decode, full size, {layout} pool, tile=1024")
     w = workloads.make_paged_decode()
     g = to_dev(w)

@@ -97,16 +97,6 @@ constexpr float kLazyRescale = 8.f;  // log2 units
 // paged grids order their work by sequence length up to this many sequences
 constexpr int kRankedMaxB = 256;
 
-// f(integral_constant<int, i>) for i = 0 .. N - 1, expanded at compile time
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Row maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950):
 // fmaxf would first quiet each input with an extra instruction.  The scores
 // are never NaN (padding rows read as zero and masked keys are -inf).

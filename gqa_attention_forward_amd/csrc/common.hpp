@@ -31,6 +31,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace gqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -148,7 +151,8 @@ __device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 3
 // clear, which keeps each 32-byte pair together, and stays below DC.
 template <int DC>
 __device__ __forceinline__ int vslot_swz(int key) {
-  static_assert(DC == 4 || DC == 8 || DC == 16 || DC == 32, "head dim 32, 64, 128 or 256");
+  static_assert(DC == 4 || DC == 8 || DC == 16 || DC == 32 || DC == 64,
+                "head dim 32, 64, 128, 256 or 512");
   if constexpr (DC >= 16)
     return ((key & 3) << 2) | (((key >> 2) & 1) << 1);
   else if constexpr (DC == 8)
@@ -164,6 +168,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, expanded at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // exp2 with the -inf convention used throughout: exp2(-inf) = 0.

@@ -417,8 +417,9 @@ def test_sweep(shape, causal, tile):
 # scalar decode at d = 256; nvfp4-megamoe-kernel commit log: head dims up to
 # 512), through every kernel form: one 16-column block (rows <= 16), two
 # (rows <= 32; two q-tiles at d = 256), the shared-tile prefill kernel at 2
-# and 4 waves (d = 32) or 4 waves (d = 256), and the split-head-dim kernel
-# (d = 512, 32 rows per workgroup)
+# and 4 waves (d = 32) or 4 waves (d = 256), and at d = 512 the split-head-dim
+# kernel (up to 32 rows per (b, kv head)) and the whole-head kernel (more
+# rows: 128 per workgroup, 37 x 4 = 148 rows in the last shape)
 SWEEP_HD = [
     # B, Hq, Hkv, Sq, Skv
     (2, 8, 2, 1, 500),

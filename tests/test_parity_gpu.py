@@ -640,10 +640,15 @@ def test_decode_sweep(Skv):
 
 # ---------------------------------------------------------------- invariants and edges
 
-def test_kvlen_one_is_exact_v0():
+# every head dim, at query lengths that reach each kernel form (4 rows per
+# kv head: stream kernel / split-head-dim d = 512 kernel; 64 rows: shared-tile
+# prefill kernel / whole-head d = 512 kernel)
+@pytest.mark.parametrize("d", [32, 64, 128, 256, 512])
+@pytest.mark.parametrize("Sq", [1, 16])
+def test_kvlen_one_is_exact_v0(d, Sq):
     """One valid key among 128 padded (NaN) rows: O is that V row, bit for bit."""
-    note("kv_len = 1, Skv = 128 NaN padded")
-    inp = workloads.make_dense(2, 8, 2, 16, 128, 128, seed=3, kv_len=[1, 1], nan_pad=True)
+    note(f"kv_len = 1, Skv = 128 NaN padded, d={d} Sq={Sq}")
+    inp = workloads.make_dense(2, 8, 2, Sq, 128, d, seed=3, kv_len=[1, 1], nan_pad=True)
     for tile in (0, 64):
         out = run_dense(inp, tile=tile, use_sink=False)
         v0 = inp["v"][:, :, :1].float().numpy()
@@ -651,9 +656,10 @@ def test_kvlen_one_is_exact_v0():
         np.testing.assert_array_equal(out, np.broadcast_to(want, out.shape))
 
 
-def test_empty_rows_are_zero_and_sink_neg_inf_is_no_sink():
-    note("kv_len = 0 rows, causal rows with no key, sink = -inf")
-    inp = workloads.make_dense(2, 4, 1, 6, 64, 64, seed=4, kv_len=[0, 3], nan_pad=True)
+@pytest.mark.parametrize("d,Sq", [(64, 6), (128, 6), (128, 40), (256, 40), (512, 6), (512, 40)])
+def test_empty_rows_are_zero_and_sink_neg_inf_is_no_sink(d, Sq):
+    note(f"kv_len = 0 rows, causal rows with no key, sink = -inf, d={d} Sq={Sq}")
+    inp = workloads.make_dense(2, 4, 1, Sq, 64, d, seed=4, kv_len=[0, 3], nan_pad=True)
     out = run_dense(inp, use_sink=False)
     assert np.all(out[0] == 0)
     outc = run_dense(inp, causal=True, use_sink=False)

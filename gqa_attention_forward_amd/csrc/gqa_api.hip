@@ -316,12 +316,15 @@ gqa_status_t gqa_attention_prefill(const void* q, const int64_t q_stride[3], con
     GQA_TRY(dispatch<false, false>(a, d, (int64_t)Sq * a.G, st));
     return ok();
   }
-  // the merge below gives empty states weight 0 without reading their O~;
-  // groups of more than 64 rows with causal or per-batch lengths have many
-  // (the sparse merge then reads only the states that hold keys)
-  a.skip_empty_o = 1;
+  // Causal groups of more than 64 rows have many empty states (splits past a
+  // q-tile's diagonal): the partial kernel leaves their O~ unwritten and the
+  // sparse merge reads only the states that hold keys.  Elsewhere every state
+  // is written (an empty one as zeros) and the merge issues all its loads in
+  // one round: short-q/long-kv (B 16, Hkv 4, 16384 keys, splits of 4096)
+  // 113-119 -> 109-112 us for the step.
+  const bool sparse = (int64_t)Sq * a.G > 64 && causal;
+  a.skip_empty_o = sparse;
   GQA_TRY(run_partial(a, d, tile_s_kv, workspace, st));
-  const bool sparse = (int64_t)Sq * a.G > 64 && (causal || kv_len);
   GQA_TRY(launch_merge(workspace, o, o_stride, B, Hq, Sq, d, a.Skv > 0 ? (int32_t)cdiv(Skv, tile_s_kv) : 1,
                        sink, st, sparse));
   return ok();
@@ -560,7 +563,9 @@ gqa_status_t paged_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   a.ws_ml = reinterpret_cast<float2*>(workspace);
   a.ws_o = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                     (size_t)Hq * total_q * n_split * 8);
-  // as for the dense split path: ragged sequences leave many states empty
+  // ragged sequences leave many states empty (the splits past a sequence's
+  // keys): their O~ stays unwritten, and the merge of groups of more than 64
+  // rows reads only the states that hold keys
   a.skip_empty_o = 1;
   GQA_TRY(dispatch<true, true>(a, d, rows, st));
   // partial rows are h * total_q + t: the merge sees B = 1, Sq = total_q

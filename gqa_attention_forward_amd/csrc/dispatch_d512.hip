@@ -2,9 +2,9 @@
 // from the other head dims.  Groups of up to 32 query rows per (b, kv head)
 // (decode, short query blocks) take the kernel that splits the head dim
 // across the four waves of a workgroup, 32 rows per workgroup; larger groups
-// (prefill) the one whose waves each own 32 rows over the whole head dim,
-// 128 rows per workgroup sharing each K/V tile.  Both run dense or paged,
-// one pass or split partials.
+// (prefill) the one whose eight waves each own 16 rows over the whole head
+// dim, 128 rows per workgroup sharing each K/V tile.  Both run dense or
+// paged, one pass or split partials.
 #include "attn_wide.hpp"
 #include "launch.hpp"
 

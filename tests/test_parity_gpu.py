@@ -262,6 +262,8 @@ APPEND_CASES = [
     (4, 16, 4, 64, [1, 2, 5, 8], [8, 64, 200, 1030]),        # short query blocks
     (3, 8, 4, 256, [1, 4, 16], [16, 300, 2000]),             # d = 256, 32 rows: two q-tiles
     (3, 8, 8, 32, [1, 7, 20], [20, 90, 700]),                # d = 32, G = 1
+    (4, 16, 4, 128, [1, 2, 3, 4], [8, 64, 200, 1030]),       # token-major pool, up to 16 rows:
+                                                             # the stream kernel's whole-row K form
 ]
 
 

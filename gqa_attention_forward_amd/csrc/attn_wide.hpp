@@ -352,9 +352,10 @@ __global__ void __launch_bounds__(256, 1) attn_wide_kernel(const AttnArgs a) {
 // accumulator file, and spill.)  The tiles go to two LDS stages by LDS DMA
 // (a 1 KiB block per 512-element row: 64 lanes x 16 bytes), requested one
 // tile ahead; the barrier that ends a tile also waits for the next one's
-// blocks.  K rows are padded by 16 bytes (the operand reads, 16 lanes over
-// 16 rows, take 16 distinct bank slots); V rows hold chunk p ^
-// vslot_swz(row) in slot p, for the transposing reads.  The stages are
+// blocks.  K rows are padded by 32 bytes: with 16 bytes the operand reads
+// (16 lanes over 16 rows) still met bank conflicts on a fifth of the
+// kernel's cycles (LDS bank-conflict counter; none with 32).  V rows hold
+// chunk p ^ vslot_swz(row) in slot p, for the transposing reads.  The stages are
 // separate static arrays, so the compiler does not wait for the DMA into
 // one before reading the other.
 struct WideRowsCfg {
@@ -365,7 +366,7 @@ struct WideRowsCfg {
   static constexpr int NC = D / 32;      // 32-wide d steps of K Q^T
   static constexpr int NDB = D / 16;     // 16-row d blocks of O^T
   static constexpr int DC = D / 8;       // 16-byte chunks per row (one DMA block)
-  static constexpr int KP = D + 8;       // K row pitch (elements)
+  static constexpr int KP = D + 16;      // K row pitch (elements)
   static constexpr int KTILE = BK * KP;
   static constexpr int VTILE = BK * D;
   static_assert(DC == 64, "one 64-lane DMA block per row");

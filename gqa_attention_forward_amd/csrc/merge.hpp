@@ -72,9 +72,11 @@ merge_kernel(const float2* __restrict__ ml, const float* __restrict__ ot, uint16
     float ov[CH][E];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int s = min(s0 + j, n_split - 1);  // branch-free: duplicates are dropped below
-      st[j] = mlr[s];
-      if constexpr (!SPARSE) load_o(s, true, ov[j]);
+      // past the last split: the identity state, and no loads (the test is
+      // wave-uniform, so the loads of a round still issue together)
+      const bool in = s0 + j < n_split;
+      st[j] = in ? mlr[s0 + j] : make_float2(-INFINITY, 0.f);
+      if constexpr (!SPARSE) load_o(s0 + j, in, ov[j]);
     }
     if constexpr (SPARSE) {
 #pragma unroll

@@ -67,8 +67,9 @@ struct StreamCfg {
   static constexpr bool Q_LDS = D > 128;
   static constexpr int QP = D + 8;
   static constexpr int QTILE = Q_LDS ? NQB * 16 * QP : 0;
-  // LDS: one V tile per wave, one combine slot per wave other than 0,
-  // (partial mode) one parked state per split of the run, and Q at d = 256
+  // LDS: one V tile per wave (and one K tile with KROW), one combine slot
+  // per wave other than 0, (partial mode) one parked state per split of the
+  // run, and Q at d = 256
   static constexpr int lds_bytes(int nw, int spw) {
     return nw * (VTILE + KTILE) * 2 + (nw - 1) * SLOT_F * 4 + spw * PEND_F * 4 + QTILE * 2;
   }

@@ -186,7 +186,7 @@ def test_spread_helpers():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("seed", [1234, 777, 4242])
+@pytest.mark.parametrize("seed", [1234, 777, 4242, 11, 22, 33])
 def test_random_shapes(seed):
     r = random.Random(seed)
     for i in range(120):
